@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+None of these re-derive the oracle's own formula: each one checks a value the
+pages print, a closed form worked out by hand, a brute-force enumeration, an
+invariant, or a special case that reduces to something simpler.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked example: n=8, K=2, d=2, F=3, two tokens.
+# Logit rows are the rows of W_g because x is one-hot.
+#   token 0 = e_0: l = [0, 3, 1, 2, -1, 0.5, 2.5, -2] -> experts (1, 6),
+#            gates (sigma(0.5), 1 - sigma(0.5))
+#   token 1 = e_1: l = [2, -1, 0, 0, 0, 1, 1, -3] -> experts (0, 5) (5 beats 6 on
+#            the tie by lower index), gates (sigma(1), 1 - sigma(1))
+# Expert weights of experts 0, 1, 5, 6 are small integers picked so that every
+# pre-activation is 0, +-1, +-2 or 5; the other experts get large weights that
+# would show up in y if a masked expert leaked in.
+# ---------------------------------------------------------------------------
+
+def hand_example():
+    n, d, F = 8, 2, 3
+    x = np.array([[1, 0], [0, 1]], np.float32)
+    wg = np.array([[0, 3, 1, 2, -1, 0.5, 2.5, -2],
+                   [2, -1, 0, 0, 0, 1, 1, -3]], np.float32)
+    w1 = np.full((n, F, d), 7.0, np.float32)
+    w3 = np.full((n, F, d), -9.0, np.float32)
+    w2 = np.full((n, d, F), 11.0, np.float32)
+    # expert 1 (token 0): w1.x = [1, 0, -1], w3.x = [2, 5, 1]
+    w1[1] = [[1, 0], [0, 1], [-1, 0]]
+    w3[1] = [[2, 0], [5, 0], [1, 1]]
+    w2[1] = [[1, 1, 1], [0, 0, 2]]
+    # expert 6 (token 0): w1.x = [0, 2, 0], w3.x = [0, 1, 0]
+    w1[6] = [[0, 0], [2, 0], [0, 0]]
+    w3[6] = [[0, 0], [1, 0], [0, 0]]
+    w2[6] = [[0, 1, 0], [0, -1, 0]]
+    # expert 0 (token 1): w1.x = [1, -2, 0], w3.x = [3, 1, 0]
+    w1[0] = [[0, 1], [0, -2], [0, 0]]
+    w3[0] = [[0, 3], [0, 1], [7, 0]]
+    w2[0] = [[1, 0, 0], [1, 1, 5]]
+    # expert 5 (token 1): w1.x = [0, 0, 1], w3.x = [0, 0, -4]
+    w1[5] = [[0, 0], [0, 0], [0, 1]]
+    w3[5] = [[0, 0], [0, 0], [0, -4]]
+    w2[5] = [[0, 0, 1], [0, 0, 0]]
+    return x, wg, w1, w3, w2
+
+
+def hand_expected():
+    silu = lambda z: z * sig(z)  # noqa: E731
+    # token 0: h1 = silu([1,0,-1]) * [2,5,1] = [2 silu(1), 0, silu(-1)]
+    #          E1 = [h1_0 + h1_1 + h1_2, 2 h1_2]
+    #          h6 = [0, silu(2) * 1, 0]; E6 = [silu(2), -silu(2)]
+    E1 = [2 * silu(1) + silu(-1), 2 * silu(-1)]
+    E6 = [silu(2), -silu(2)]
+    g = sig(0.5)
+    y0 = [g * E1[j] + (1 - g) * E6[j] for j in range(2)]
+    # token 1: h0 = silu([1,-2,0]) * [3,1,0] = [3 silu(1), silu(-2), 0]
+    #          E0 = [h0_0, h0_0 + h0_1 + 5 h0_2]
+    #          h5 = [0, 0, silu(1) * -4]; E5 = [-4 silu(1), 0]
+    E0 = [3 * silu(1), 3 * silu(1) + silu(-2)]
+    E5 = [-4 * silu(1), 0.0]
+    g = sig(1.0)
+    y1 = [g * E0[j] + (1 - g) * E5[j] for j in range(2)]
+    return dict(idx=[[1, 6], [0, 5]], gates=[[sig(0.5), 1 - sig(0.5)], [sig(1.0), 1 - sig(1.0)]],
+                y=[y0, y1], counts=[1, 1, 0, 0, 0, 1, 1, 0])
+
+
+def test_hand_worked_example():
+    out = oracle.moe_layer(*hand_example(), K=2)
+    exp = hand_expected()
+    np.testing.assert_array_equal(out["idx"], exp["idx"])
+    np.testing.assert_array_equal(out["counts"], exp["counts"])
+    np.testing.assert_allclose(out["gates"], exp["gates"], rtol=1e-6, atol=0)
+    np.testing.assert_allclose(out["y"], exp["y"], rtol=2e-6, atol=1e-6)
+
+
+def test_hand_example_sparse_path_matches():
+    """The reference layouts (group -> expert rows -> combine) give the same y."""
+    x, wg, w1, w3, w2 = hand_example()
+    for tile_m in (1, 4):
+        out = oracle.moe_layer(x, wg, w1, w3, w2, K=2)
+        grp = oracle.group_by_expert(out["idx"], 8, tile_m)
+        _, y_perm = oracle.expert_rows(x, grp["row_src"], grp["offsets"], w1, w3, w2, K=2)
+        y = oracle.combine(y_perm, grp["row_of"], out["gates"])
+        np.testing.assert_allclose(y, hand_expected()["y"], rtol=2e-6, atol=1e-6)
+
+
+def test_silu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 2.0, 30.0, -30.0, -200.0], np.float32)
+    got = oracle.silu(z)
+    exp = [0.0, sig(1), -sig(-1) * 1, 2 * sig(2), 30.0, -30.0 * sig(-30.0), 0.0]
+    np.testing.assert_allclose(got, exp, rtol=1e-6, atol=1e-30)
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.7310585786300049) < 1e-7
+
+
+def test_routing_margin_hand():
+    x, wg, *_ = hand_example()
+    np.testing.assert_array_equal(oracle.routing_margin(x, wg), [0.5, 0.0])
+    np.testing.assert_array_equal(oracle.top_gap(x, wg), [0.5, 1.0])
+
+
+# ---------------------------------------------------------------------------
+# Top-2 by brute force
+# ---------------------------------------------------------------------------
+
+def _key_beats(l, i, j):
+    """Expert i is ordered before expert j: larger logit, or equal and lower index."""
+    return l[i] > l[j] or (l[i] == l[j] and i < j)
+
+
+@pytest.mark.parametrize("grid", [None, 1.0, 0.25])
+def test_top2_brute_force(grid):
+    rng = np.random.default_rng(123)
+    n = 8
+    logits = rng.standard_normal((400, n)).astype(np.float32)
+    if grid is not None:  # coarse grid -> many exact ties
+        logits = (np.round(logits / grid) * grid).astype(np.float32)
+    idx = oracle.topk_indices(logits, 2)
+    for t in range(logits.shape[0]):
+        l = logits[t]
+        winners = [pair for pair in itertools.combinations(range(n), 2)
+                   if all(_key_beats(l, a, b) for a in pair for b in range(n) if b not in pair)]
+        assert len(winners) == 1
+        assert set(idx[t]) == set(winners[0])
+        assert _key_beats(l, idx[t, 0], idx[t, 1])
+
+
+def test_top2_scale_invariance():
+    inp = mi.make_layer(64, 32, 16, dtype="f32", init="fanin", seed=3, workload=101)
+    x, wg, *_ = inp.numpy_f32()
+    idx = oracle.gating(x, wg)[1]
+    for s in (2.0, 0.5, 1024.0):
+        np.testing.assert_array_equal(oracle.gating(x, wg * np.float32(s))[1], idx)
+
+
+# ---------------------------------------------------------------------------
+# Gate invariants
+# ---------------------------------------------------------------------------
+
+def test_gate_invariants():
+    inp = mi.make_layer(256, 64, 32, dtype="f32", init="fanin", seed=5, workload=102)
+    x, wg, *_ = inp.numpy_f32()
+    G, idx, _ = oracle.gating(x, wg)
+    assert ((G != 0).sum(axis=1) == 2).all()
+    assert (G >= 0).all()
+    np.testing.assert_allclose(G.sum(axis=1), 1.0, rtol=0, atol=2.0 ** -22)
+    rows = np.arange(G.shape[0])
+    assert (G[rows, idx[:, 0]] >= 0.5).all() and (G[rows, idx[:, 1]] <= 0.5).all()
+
+
+def test_zero_router_tie():
+    x = np.random.default_rng(0).standard_normal((5, 16)).astype(np.float32)
+    wg = np.zeros((16, 8), np.float32)
+    G, idx, _ = oracle.gating(x, wg)
+    np.testing.assert_array_equal(idx, np.tile([0, 1], (5, 1)))
+    np.testing.assert_array_equal(G[:, :2], 0.5)
+    np.testing.assert_array_equal(G[:, 2:], 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Layer special cases
+# ---------------------------------------------------------------------------
+
+def _small(seed, T=24, d=32, F=48):
+    inp = mi.make_layer(T, d, F, dtype="f32", init="fanin", seed=seed, workload=103)
+    return inp.numpy_f32()
+
+
+@pytest.mark.parametrize("a", [0, 3, 7])
+def test_single_expert_dominance_bitwise(a):
+    x, wg, w1, w3, w2 = _small(7)
+    x = x.copy()
+    wg = wg.copy()
+    x[:, 0] = 1.0
+    wg[0, a] = 1e4  # l_a - l_b >= ~1e4: exp(l_b - l_a) underflows to exactly 0
+    out = oracle.moe_layer(x, wg, w1, w3, w2)
+    assert (out["idx"][:, 0] == a).all()
+    assert (out["gates"][:, 0] == 1.0).all() and (out["gates"][:, 1] == 0.0).all()
+    Ea = oracle.swiglu_expert(x, w1[a], w3[a], w2[a])
+    assert np.array_equal(out["y"], Ea)
+
+
+def test_identical_experts():
+    x, wg, w1, w3, w2 = _small(8)
+    w1 = np.repeat(w1[:1], 8, axis=0)
+    w3 = np.repeat(w3[:1], 8, axis=0)
+    w2 = np.repeat(w2[:1], 8, axis=0)
+    out = oracle.moe_layer(x, wg, w1, w3, w2)
+    E = oracle.swiglu_expert(x, w1[0], w3[0], w2[0])
+    np.testing.assert_allclose(out["y"], E, rtol=1e-5, atol=1e-6 * np.abs(E).max())
+
+
+def test_token_permutation_equivariance():
+    x, wg, w1, w3, w2 = _small(9)
+    perm = np.random.default_rng(1).permutation(x.shape[0])
+    a = oracle.moe_layer(x, wg, w1, w3, w2)
+    b = oracle.moe_layer(x[perm], wg, w1, w3, w2)
+    np.testing.assert_array_equal(b["idx"], a["idx"][perm])
+    np.testing.assert_allclose(b["y"], a["y"][perm], rtol=1e-5, atol=1e-6)
+
+
+def test_expert_relabelling_invariance():
+    x, wg, w1, w3, w2 = _small(10)
+    p = np.array([5, 2, 7, 0, 3, 6, 1, 4])  # new expert j is old expert p[j]
+    a = oracle.moe_layer(x, wg, w1, w3, w2)
+    b = oracle.moe_layer(x, wg[:, p], w1[p], w3[p], w2[p])
+    assert oracle.routing_margin(x, wg).min() > 0 and oracle.top_gap(x, wg).min() > 0
+    np.testing.assert_array_equal(p[b["idx"]], a["idx"])
+    np.testing.assert_array_equal(b["counts"], a["counts"][p])
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-5, atol=1e-6)
+
+
+def test_fp64_loop_bound():
+    """fp32 oracle within 1e-5 (per-token relative) of a float64 evaluation
+    written as explicit loops over the selected experts."""
+    x, wg, w1, w3, w2 = _small(11, T=6, d=8, F=12)
+    out = oracle.moe_layer(x, wg, w1, w3, w2)
+    x64, w1_, w3_, w2_ = (a.astype(np.float64) for a in (x, w1, w3, w2))
+    for t in range(x.shape[0]):
+        l = [sum(float(x[t, k]) * float(wg[k, e]) for k in range(8)) for e in range(8)]
+        order = sorted(range(8), key=lambda e: (-l[e], e))[:2]
+        m = max(l[e] for e in order)
+        z = sum(math.exp(l[e] - m) for e in order)
+        y = [0.0] * 8
+        for e in order:
+            g = math.exp(l[e] - m) / z
+            h = []
+            for f in range(12):
+                a = sum(x64[t, k] * w1_[e, f, k] for k in range(8))
+                b = sum(x64[t, k] * w3_[e, f, k] for k in range(8))
+                h.append(a / (1 + math.exp(-a)) * b)
+            for j in range(8):
+                y[j] += g * sum(w2_[e, j, f] * h[f] for f in range(12))
+        err = np.abs(out["y"][t] - np.array(y)).max() / np.abs(y).max()
+        assert err < 1e-5
+        assert sorted(order) == sorted(out["idx"][t].tolist())
+
+
+# ---------------------------------------------------------------------------
+# Reference layouts
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile_m", [1, 16, 128])
+def test_group_by_expert_properties(tile_m):
+    rng = np.random.default_rng(tile_m)
+    T, K, n = 300, 2, 8
+    idx = np.stack([rng.permutation(n)[:K] for _ in range(T)]).astype(np.int32)
+    g = oracle.group_by_expert(idx, n, tile_m)
+    counts, offsets, row_src, row_of = g["counts"], g["offsets"], g["row_src"], g["row_of"]
+    assert counts.sum() == T * K
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=n))
+    assert offsets[0] == 0 and (np.diff(offsets) % tile_m == 0).all()
+    assert (np.diff(offsets) >= counts).all() and (np.diff(offsets) < counts + tile_m).all()
+    assert len(row_src) == T * K + n * (tile_m - 1)
+    for e in range(n):
+        seg = row_src[offsets[e]:offsets[e + 1]]
+        real = seg[:counts[e]]
+        assert (seg[counts[e]:] == -1).all()
+        assert (np.diff(real) > 0).all()
+        assert (idx.ravel()[real] == e).all()
+    assert (row_src[offsets[n]:] == -1).all()
+    flat_of = row_of.ravel()
+    np.testing.assert_array_equal(row_src[flat_of], np.arange(T * K))
+
+
+def test_sparse_path_equals_dense():
+    x, wg, w1, w3, w2 = _small(12, T=40)
+    out = oracle.moe_layer(x, wg, w1, w3, w2)
+    g = oracle.group_by_expert(out["idx"], 8, 16)
+    _, y_perm = oracle.expert_rows(x, g["row_src"], g["offsets"], w1, w3, w2)
+    y = oracle.combine(y_perm, g["row_of"], out["gates"])
+    np.testing.assert_allclose(y, out["y"], rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm, bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_closed_form():
+    h = np.array([[3.0, 4.0], [-2.0, -2.0], [0.0, 0.0]], np.float32)
+    x = oracle.rmsnorm(h, eps=1e-5)
+    np.testing.assert_allclose(x[0], np.array([3, 4]) / math.sqrt(12.5 + 1e-5), rtol=1e-6)
+    np.testing.assert_allclose(x[1], -2 / math.sqrt(4 + 1e-5), rtol=1e-6)
+    np.testing.assert_array_equal(x[2], 0.0)
+    big = np.random.default_rng(0).standard_normal((4, 4096)).astype(np.float32) * 7
+    np.testing.assert_allclose((oracle.rmsnorm(big) ** 2).mean(axis=1), 1.0, rtol=1e-5)
+
+
+def test_round_bf16():
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -20), 3.0e-39], np.float32)
+    np.testing.assert_array_equal(oracle.round_bf16(v)[:4], [1.0, 1.0, 1 + 2 ** -6, -(1 + 2 ** -7)])
+    r = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 100
+    ref = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(r), ref)
+
+
+def test_moe_block_residual():
+    x, wg, w1, w3, w2 = _small(13)
+    h_next, out = oracle.moe_block(x, wg, w1, w3, w2, bf16_storage=False)
+    xn = oracle.rmsnorm(x)
+    ref = oracle.moe_layer(xn, wg, w1, w3, w2)["y"]
+    np.testing.assert_allclose(h_next - x, ref, rtol=1e-4, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# The pages' printed parameter counts
+# ---------------------------------------------------------------------------
+
+def test_parameter_counts_golden():
+    with open(os.path.join(GOLDEN, "mixtral_param_counts.json")) as f:
+        g = json.load(f)
+    for wl in mi.WORKLOADS[1:]:
+        d, F, n = wl["d"], wl["F"], wl["n"]
+        assert (d, F, n, wl["K"]) == (g["dims"]["d_model"], g["dims"]["d_ffn"],
+                                      g["dims"]["n_experts"], g["dims"]["top_k"])
+        small = mi.make_layer(2, 16, 24, n=n, dtype="bf16", seed=0, workload=104)
+        # shapes follow [n, F, d] / [n, d, F] / [d, n] whatever the sizes
+        assert small.w1.shape == (n, 24, 16) and small.w3.shape == (n, 24, 16)
+        assert small.w2.shape == (n, 16, 24) and small.wg.shape == (16, n)
+        per_expert = F * d + F * d + d * F
+        per_layer = n * per_expert
+        L = g["dims"]["n_layers"]
+        assert round(per_expert / 1e6, 2) == g["printed"]["per_expert_millions"]
+        assert round(per_layer / 1e9, 3) == g["printed"]["per_layer_billions"]
+        assert round(L * per_layer / 1e9, 1) == g["printed"]["all_layers_billions"]
+        assert round(L * d * n / 1e6, 2) == g["printed"]["router_all_layers_millions"]
+    assert mi.WORKLOADS[4]["layers"] == g["dims"]["n_layers"]
+
+
+def test_tiny_workload_runs_fast():
+    inp = mi.make_workload(0)
+    out = oracle.moe_layer(*inp.numpy_f32())
+    assert out["y"].shape == (64, 128) and out["counts"].sum() == 128
