@@ -1,0 +1,306 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and
+// launch sequencing.  Every entry point validates synchronously, enqueues its
+// kernels on the caller's stream and returns without synchronising.
+#include <new>
+
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+namespace {
+
+constexpr int32_t kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int dtype_size(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+// Shape checks shared by every call.
+moe_status_t check_desc(const moe_layer_desc_t* d) {
+    if (d == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->d_model <= 0 || d->d_ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (d->top_k > d->n_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->weight_dtype != MOE_F32 && d->weight_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->d_model % 8 != 0 || d->d_ffn % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->act_dtype != d->weight_dtype) return MOE_ERR_UNSUPPORTED;
+    if (d->n_experts != 8 || d->top_k != 2) return MOE_ERR_UNSUPPORTED;
+    if (d->act_dtype == MOE_BF16 && (d->d_model % 512 != 0 || d->d_ffn % 512 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_T(int32_t T, const moe_layer_desc_t* d) {
+    if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+    // Permuted row indices and T*K assignment ids are int32.
+    const long long P = static_cast<long long>(T) * d->top_k + static_cast<long long>(d->n_experts) * 255;
+    if (P > 0x7fffffffLL) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+int default_tile(const moe_layer_desc_t* d, int32_t T) {
+    if (d->act_dtype != MOE_BF16) return 16;
+    return T <= 64 ? 16 : 256;
+}
+
+moe_status_t check_tile(const moe_layer_desc_t* d, int32_t tile_m) {
+    if (tile_m == 16) return MOE_OK;
+    if (tile_m == 256) return d->act_dtype == MOE_BF16 ? MOE_OK : MOE_ERR_UNSUPPORTED;
+    return MOE_ERR_INVALID_ARGUMENT;
+}
+
+long long pmax(const moe_layer_desc_t* d, int32_t T, int32_t tile_m) {
+    return static_cast<long long>(T) * d->top_k + static_cast<long long>(d->n_experts) * (tile_m - 1);
+}
+
+moe::Shape shape_of(const moe_layer_desc_t* d, int32_t T) {
+    return moe::Shape{T, d->d_model, d->d_ffn, d->n_experts, d->top_k, d->act_dtype == MOE_BF16};
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace carving of moe_layer_forward.
+struct LayerWs {
+    int32_t* idx;
+    float* gate;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* row_src;
+    int32_t* row_of;
+    void* h;
+    float* y_perm;
+    size_t bytes;
+};
+
+LayerWs carve_layer(const moe_layer_desc_t* d, int32_t T, int32_t tile_m, char* base) {
+    LayerWs w{};
+    const size_t TK = static_cast<size_t>(T) * d->top_k;
+    const size_t P = static_cast<size_t>(pmax(d, T, tile_m));
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base == nullptr ? nullptr : base + off;
+        off += align_up(bytes);
+        return p;
+    };
+    w.idx = reinterpret_cast<int32_t*>(take(TK * 4));
+    w.gate = reinterpret_cast<float*>(take(TK * 4));
+    w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(d->n_experts) * 4));
+    w.offsets = reinterpret_cast<int32_t*>(take(static_cast<size_t>(d->n_experts + 1) * 4));
+    w.row_src = reinterpret_cast<int32_t*>(take(P * 4));
+    w.row_of = reinterpret_cast<int32_t*>(take(TK * 4));
+    w.h = take(P * static_cast<size_t>(d->d_ffn) * dtype_size(d->act_dtype));
+    w.y_perm = reinterpret_cast<float*>(take(P * static_cast<size_t>(d->d_model) * 4));
+    w.bytes = off;
+    return w;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+int32_t moe_version(void) { return kVersion; }
+
+int32_t moe_default_tile_m(const moe_layer_desc_t* desc, int32_t T) {
+    if (check_desc(desc) != MOE_OK || T < 0) return 0;
+    return default_tile(desc, T);
+}
+
+int64_t moe_max_permuted_rows(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m) {
+    if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return -1;
+    if (tile_m == 0) tile_m = default_tile(desc, T);
+    if (check_tile(desc, tile_m) != MOE_OK) return -1;
+    return pmax(desc, T, tile_m);
+}
+
+size_t moe_workspace_size(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m) {
+    if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return 0;
+    if (tile_m == 0) tile_m = default_tile(desc, T);
+    if (check_tile(desc, tile_m) != MOE_OK) return 0;
+    return carve_layer(desc, T, tile_m, nullptr).bytes;
+}
+
+moe_status_t moe_router_topk(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                             const float* w_gate, int32_t* topk_idx, float* topk_gate,
+                             float* logits_out, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (x == nullptr || w_gate == nullptr || topk_idx == nullptr || topk_gate == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_router_topk(shape_of(desc, T), x, w_gate, topk_idx, topk_gate,
+                                              logits_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m,
+                         const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                         int32_t* row_src, int32_t* row_of, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if (counts == nullptr || offsets == nullptr || row_src == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (topk_idx == nullptr || row_of == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    // T == 0 still writes counts = 0, offsets = 0 and the all-padding row_src.
+    return hip_status(moe::launch_permute(shape_of(desc, T), tile_m, topk_idx, counts, offsets,
+                                          row_src, row_of, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_gate_up(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m,
+                                const void* x, const int32_t* row_src, const int32_t* counts,
+                                const int32_t* offsets, const void* w1, const void* w3, void* h,
+                                void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (x == nullptr || row_src == nullptr || counts == nullptr || offsets == nullptr ||
+        w1 == nullptr || w3 == nullptr || h == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w3) || !aligned16(h))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_gate_up(shape_of(desc, T), tile_m, x, row_src, counts, offsets,
+                                          w1, w3, h, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_down(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m,
+                             const void* h, const int32_t* counts, const int32_t* offsets,
+                             const void* w2, float* y_perm, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (h == nullptr || counts == nullptr || offsets == nullptr || w2 == nullptr || y_perm == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(h) || !aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_down(shape_of(desc, T), tile_m, h, counts, offsets, w2, y_perm,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_swiglu(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m,
+                                const void* x, const int32_t* row_src, const int32_t* counts,
+                                const int32_t* offsets, const void* w1, const void* w3,
+                                const void* w2, void* h, float* y_perm, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (w2 == nullptr || y_perm == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    s = moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, h, stream);
+    if (s != MOE_OK) return s;
+    return moe_expert_down(desc, T, tile_m, h, counts, offsets, w2, y_perm, stream);
+}
+
+moe_status_t moe_combine(const moe_layer_desc_t* desc, int32_t T, const float* y_perm,
+                         const int32_t* row_of, const float* topk_gate, const void* residual,
+                         void* y, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (y_perm == nullptr || row_of == nullptr || topk_gate == nullptr || y == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(y_perm) || !aligned16(y) || (residual != nullptr && !aligned16(residual)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_combine(shape_of(desc, T), y_perm, row_of, topk_gate, residual, y,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_rmsnorm(int32_t T, int32_t d, int32_t dtype, const void* h, float eps,
+                         void* x_out, void* stream) {
+    if (T < 0 || d <= 0 || d % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (h == nullptr || x_out == nullptr || h == x_out) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(h) || !aligned16(x_out)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_rmsnorm(T, d, dtype == MOE_BF16, h, eps, x_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                               const float* w_gate, const void* w1, const void* w3,
+                               const void* w2, const void* residual, void* y,
+                               int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (x == nullptr || w_gate == nullptr || w1 == nullptr || w3 == nullptr || w2 == nullptr ||
+        y == nullptr || workspace == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (x == y) return MOE_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) ||
+        !aligned16(y) || (residual != nullptr && !aligned16(residual)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const int tile_m = default_tile(desc, T);
+    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
+    if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    const moe::Shape sh = shape_of(desc, T);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
+    float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
+    int32_t* counts = counts_out != nullptr ? counts_out : w.counts;
+    hipError_t e;
+    if ((e = moe::launch_router_topk(sh, x, w_gate, idx, gate, nullptr, st)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if ((e = moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, w1, w3, w.h, st)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if ((e = moe::launch_down(sh, tile_m, w.h, counts, w.offsets, w2, w.y_perm, st)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if ((e = moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+size_t moe_block_workspace_size(const moe_layer_desc_t* desc, int32_t T) {
+    if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return 0;
+    const size_t xn = align_up(static_cast<size_t>(T) * desc->d_model * dtype_size(desc->act_dtype));
+    return xn + carve_layer(desc, T, default_tile(desc, T), nullptr).bytes;
+}
+
+moe_status_t moe_block_forward(const moe_layer_desc_t* desc, int32_t T, const void* h,
+                               float eps, const float* w_gate, const void* w1, const void* w3,
+                               const void* w2, void* h_out, int32_t* topk_idx_out,
+                               int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+    if (T == 0) return MOE_OK;
+    if (h == nullptr || h_out == nullptr || workspace == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = moe_block_workspace_size(desc, T);
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const size_t xn = align_up(static_cast<size_t>(T) * desc->d_model * dtype_size(desc->act_dtype));
+    char* ws = static_cast<char*>(workspace);
+    s = moe_rmsnorm(T, desc->d_model, desc->act_dtype, h, eps, ws, stream);
+    if (s != MOE_OK) return s;
+    return moe_layer_forward(desc, T, ws, w_gate, w1, w3, w2, h, h_out, topk_idx_out, nullptr,
+                             counts_out, ws + xn, workspace_bytes - xn, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Shared device helpers and the internal launcher interface of the gfx950 MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an IEEE fp32)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Widen the 8 bf16 values held in a 16-byte word.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// SiLU(z) = z * sigmoid(z) in fp32 with the accurate exp.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Internal launchers (host side).  Each enqueues on `stream` and returns the
+// hipGetLastError() status of its launches.  Shapes are validated by the ABI.
+// ---------------------------------------------------------------------------
+struct Shape {
+    int T, d, F, n, K;
+    bool bf16;
+};
+
+hipError_t launch_router_topk(const Shape& s, const void* x, const float* wg, int32_t* idx,
+                              float* gate, float* logits, hipStream_t st);
+
+hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* row_src, int32_t* row_of, hipStream_t st);
+
+// Grouped SwiGLU projections.  tile_m selects the kernel family.
+hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32_t* row_src,
+                          const int32_t* counts, const int32_t* offsets, const void* w1,
+                          const void* w3, void* h, hipStream_t st);
+hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
+                       const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st);
+
+hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
+                          const float* gate, const void* residual, void* y, hipStream_t st);
+
+hipError_t launch_rmsnorm(int T, int d, bool bf16, const void* h, float eps, void* x_out,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,126 @@
+// Dropless grouping of the T*K routing assignments by expert: histogram,
+// exclusive scan into tile-padded segment offsets, stable scatter.
+//
+// Mixtral routes every token to its two experts with no capacity limit and no
+// dropping (paper-graph-ui page, section 3.4 "Top-K Gating Mechanism and
+// Routing", load-balancing paragraph) and runs all experts' tokens as one packed
+// matrix (same section, "Megablocks kernels" paragraph).  The grouped GEMMs need
+// each expert's rows contiguous and padded to their row-tile size.
+//
+// One block of 1024 threads.  Thread i owns the contiguous assignment range
+// [i*per, (i+1)*per), so scattering each thread's assignments in order at its
+// exclusive prefix keeps ascending assignment order inside a segment: the
+// result is deterministic and matches a stable sort by expert.
+#include "moe_common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kExperts = 8;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int TK,
+                                                           int tile_m, int P_max,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ row_src,
+                                                           int32_t* __restrict__ row_of) {
+    __shared__ int s_wave[kWaves][kExperts];
+    __shared__ int s_total[kExperts];
+    __shared__ int s_off[kExperts + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int per = (TK + kThreads - 1) / kThreads;
+    const int a0 = min(TK, tid * per);
+    const int a1 = min(TK, a0 + per);
+
+    int c[kExperts];
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) c[e] = 0;
+    for (int a = a0; a < a1; ++a) {
+        const int e = idx[a];
+#pragma unroll
+        for (int j = 0; j < kExperts; ++j) c[j] += (e == j) ? 1 : 0;
+    }
+
+    // Inclusive scan of each expert's count across the wave.
+    int incl[kExperts];
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+        int v = c[e];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(v, off, 64);
+            if (lane >= off) v += u;
+        }
+        incl[e] = v;
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int e = 0; e < kExperts; ++e) s_wave[wave][e] = incl[e];
+    }
+    __syncthreads();
+    if (tid < kExperts) {
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int v = s_wave[w][tid];
+            s_wave[w][tid] = run;
+            run += v;
+        }
+        s_total[tid] = run;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int off = 0;
+        for (int e = 0; e < kExperts; ++e) {
+            s_off[e] = off;
+            counts[e] = s_total[e];
+            offsets[e] = off;
+            off += (s_total[e] + tile_m - 1) / tile_m * tile_m;
+        }
+        s_off[kExperts] = off;
+        offsets[kExperts] = off;
+    }
+    __syncthreads();
+
+    int pos[kExperts];
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) pos[e] = s_off[e] + s_wave[wave][e] + incl[e] - c[e];
+    for (int a = a0; a < a1; ++a) {
+        const int e = idx[a];
+        int p = -1;
+#pragma unroll
+        for (int j = 0; j < kExperts; ++j) {
+            if (e == j) {
+                p = pos[j];
+                pos[j] = p + 1;
+            }
+        }
+        if (p >= 0) row_src[p] = a;
+        row_of[a] = p;
+    }
+
+    // Padding rows of every segment, then everything past the last segment.
+    for (int e = 0; e < kExperts; ++e) {
+        const int lo = s_off[e] + s_total[e];
+        const int hi = s_off[e + 1];
+        for (int p = lo + tid; p < hi; p += kThreads) row_src[p] = -1;
+    }
+    for (int p = s_off[kExperts] + tid; p < P_max; p += kThreads) row_src[p] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* row_src, int32_t* row_of, hipStream_t st) {
+    const int TK = s.T * s.K;
+    const int P_max = TK + s.n * (tile_m - 1);
+    permute_kernel<<<1, kThreads, 0, st>>>(idx, TK, tile_m, P_max, counts, offsets, row_src, row_of);
+    return hipGetLastError();
+}
+
+}  // namespace moe
