@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""MoE-layer tokens/s on one MI355X, with the roofline of the dominant kernel.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny]
+
+One step is one pass of the whole layer (router -> permute -> gate/up + SwiGLU ->
+down -> combine) over one batch of synthetic tokens already resident in HBM.
+Phase A times K steps of moe_layer_forward between device synchronisations
+(the reported value).  Phase B runs K more steps through the individual entry
+points with HIP events around each stage, recorded on the stream the kernels
+run on, which gives each kernel's average duration for the roofline figure.
+The CPU oracle is then timed on a bounded sample of the same workload.
+
+Prints one JSON line.  Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 MI355X + % of HBM (decode) / MFMA (prefill) roofline"
+WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3}
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_way_amd", "csrc", "grouped_gemm.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time spent timing the CPU oracle (0 skips it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary, or None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != source_digest(GEMM_SRC):
+        return None
+    return float(m.group(1))
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": 5}))
+
+
+def cpu_baseline(inp, seconds: float, rows_cap: int):
+    """The oracle, as it stands, on a bounded sample of the workload's tokens."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    xn, wgn, w1n, w3n, w2n = inp.numpy_f32()
+    T = xn.shape[0]
+    rows = np.arange(min(T, rows_cap))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_layer(xn[rows], wgn, w1n, w3n, w2n)
+        done += rows.size
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} of {T} tokens per call (dense fp32, all 8 experts), "
+                      f"{done // rows.size} calls in {el:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import moe_inputs as mi
+    import sparse_moe_transformer_way_amd as moe
+
+    wl = WORKLOADS[args.workload]
+    spec = mi.WORKLOADS[wl]
+    inp = mi.make_workload(wl, seed=args.seed)
+    T, d, F, n, K = inp.T, inp.d, inp.F, inp.n, inp.K
+    dt = torch.float32 if inp.dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda")
+    x, wg, w1, w3, w2 = (t.to(dev) for t in (inp.x, inp.wg, inp.w1, inp.w3, inp.w2))
+    desc = moe.make_desc(d, F, n, K, dtype=dt)
+    tile_m = moe.moe_default_tile_m(desc, T)
+    P = moe.moe_max_permuted_rows(desc, T, tile_m)
+
+    # outputs and scratch, allocated before any timing
+    y = torch.empty((T, d), dtype=dt, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(P, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, K), dtype=torch.int32, device=dev)
+    h = torch.empty((P, F), dtype=dt, device=dev)
+    y_perm = torch.empty((P, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_workspace_size(desc, T, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def layer_step():
+        moe.moe_layer_forward(desc, x, wg, w1, w3, w2, y=y, topk_idx_out=idx, topk_gate_out=gate,
+                              counts_out=counts, workspace=ws, stream=stream)
+
+    stages = ["router_topk", "permute", "expert_gate_up", "expert_down", "combine"]
+
+    def staged_step(ev):
+        ev[0].record(stream)
+        moe.moe_router_topk(desc, x, wg, idx, gate, stream=stream)
+        ev[1].record(stream)
+        moe.moe_permute(desc, idx, tile_m, counts, offsets, row_src, row_of, stream=stream)
+        ev[2].record(stream)
+        moe.moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, h, stream=stream)
+        ev[3].record(stream)
+        moe.moe_expert_down(desc, T, tile_m, h, counts, offsets, w2, y_perm, stream=stream)
+        ev[4].record(stream)
+        moe.moe_combine(desc, y_perm, row_of, gate, y=y, stream=stream)
+        ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        layer_step()
+    torch.cuda.synchronize()
+
+    # Phase A: the reported value
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer_step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # Phase B: per-kernel durations from HIP events on the kernels' stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    tb0 = time.perf_counter()
+    for s in range(args.steps):
+        staged_step(evs[s])
+    torch.cuda.synchronize()
+    staged_ms = 1e3 * (time.perf_counter() - tb0) / args.steps
+    stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, name in enumerate(stages)}
+
+    cnt = counts.cpu().tolist()
+    touched = sum(1 for c in cnt if c > 0)
+    TK = T * K
+    esz = 2 if dt == torch.bfloat16 else 4
+    # algorithmic work of the dominant kernel (gate/up + SwiGLU): per touched
+    # expert 2*F*d weights, plus the gathered rows read and h written
+    gu_bytes = touched * 2 * F * d * esz + TK * d * esz + TK * F * esz
+    gu_flops = 4.0 * TK * d * F
+    layer_bytes = touched * 3 * F * d * esz + 2 * T * d * esz + d * n * 4
+    layer_flops = 2.0 * TK * 3 * d * F + 2.0 * T * d * n
+    gu_s = stage_ms["expert_gate_up"] / 1e3
+    bound = "hbm" if (T * K) / max(1, touched) < 64 else "mfma"
+    kern_name = ("gate_up_stream" if tile_m == 16 else "gate_up_tiled") if dt == torch.bfloat16 else "gate_up_f32"
+    if bound == "hbm":
+        achieved = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = stored_traffic(kern_name, spec["name"])
+    roof["kernel"] = kern_name
+    roof["kernel_ms"] = round(stage_ms["expert_gate_up"], 4)
+    roof["algorithmic_per_launch"] = gu_bytes if bound == "hbm" else gu_flops
+
+    value = T / (ms_per_step / 1e3)
+    layer_s = ms_per_step / 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec["name"], "T": T, "d_model": d, "d_ffn": F, "n_experts": n,
+                   "top_k": K, "tile_m": tile_m, "expert_counts": cnt},
+        "roofline": roof,
+        "layer": {"hbm_GBs": round(layer_bytes / layer_s / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_TFLOPs": round(layer_flops / layer_s / 1e12, 1),
+                  "mfma_frac": round(layer_flops / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "staged_ms_per_step": round(staged_ms, 4),
+                  "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, rows_cap=32 if wl <= 1 else 64)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,9 +22,12 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -disable-promote-alloca-to-lds: private arrays never silently take LDS (the
+# tiled kernels budget all of it themselves).
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I", os.path.join(ROOT, "include"),
 ]
 

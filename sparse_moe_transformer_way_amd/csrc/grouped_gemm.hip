@@ -19,10 +19,8 @@
 //     rows of one expert; its 4 waves split K, stream their weights straight
 //     into MFMA registers (no LDS staging: each weight is used by at most a few
 //     row blocks) and reduce through LDS.  Experts with no rows are skipped.
-//   * tiled (tile_m 256, bf16): many rows per expert, MFMA-bound.  256x256
-//     output tiles (weight rows x token rows), 4 waves of 128x128 with
-//     v_mfma_f32_32x32x16_bf16, BK = 64, LDS double buffer staged through
-//     registers, XOR-swizzled 16-byte chunks, XCD-grouped tile order.
+//   * tiled (tile_m 256, bf16): many rows per expert, MFMA-bound; in
+//     tiled_gemm.hip.
 //   * fp32 (tile_m 16): plain LDS-tiled FMA kernel for fp32 layers.
 #include "moe_common.h"
 
@@ -201,193 +199,6 @@ __global__ __launch_bounds__(256) void stream_kernel(
 }
 
 // ===========================================================================
-// LDS-tiled MFMA kernel (bf16, tile_m = 256)
-// ===========================================================================
-
-constexpr int kTW = 256;  // weight rows per tile
-constexpr int kTT = 256;  // token rows per tile
-constexpr int kBK = 64;   // k per stage (8 chunks of 16 bytes)
-
-// Byte-chunk swizzle of a 128-byte LDS row.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
-
-template <bool DUAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_kernel(
-    const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
-    int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_tt, int n_wt,
-    int ld_out, int n_src, int P) {
-    __shared__ uint4 lds_w[2][kTW * 8];
-    __shared__ uint4 lds_t[2][kTT * 8];
-
-    // XCD-grouped order: blocks b, b+8, b+16, ... run on the same XCD; give
-    // each XCD a contiguous range of tiles (token tile fastest).
-    const int G = gridDim.x;
-    const int xcd = blockIdx.x & 7;
-    const int L = xcd * (G >> 3) + (blockIdx.x >> 3);
-    if (L >= n_tt * n_wt) return;
-    const int tt = L % n_tt;
-    const int wt = L / n_tt;
-
-    const int p0 = tt * kTT;
-    if (p0 >= offsets[kExperts]) return;
-    const int e = expert_of_row(offsets, p0);
-    // rows of this tile that may be written (segment end, clamped to the buffers)
-    const int row_end = min(offsets[e + 1], P);
-    const int valid = min(min(kTT, offsets[e] + counts[e] - p0), row_end - p0);
-    if (valid <= 0) return;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wave_w = wave & 1;
-    const int wave_t = wave >> 1;
-
-    // ---- global -> register staging assignment: 8 weight rows + 8 token rows per thread
-    const int c = tid & 7;
-    const int r0 = tid >> 3;
-    const bf16_t* gw[8];
-    const bf16_t* gt[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int rw = r0 + 32 * i;
-        if (DUAL) {
-            const int f0 = wt * (kTW / 2);
-            const bf16_t* base = (rw < kTW / 2) ? wa : wb;
-            gw[i] = base + (static_cast<size_t>(e) * Nw + f0 + (rw & (kTW / 2 - 1))) * Kdim + 8 * c;
-        } else {
-            gw[i] = wa + (static_cast<size_t>(e) * Nw + wt * kTW + rw) * Kdim + 8 * c;
-        }
-        const int rt = r0 + 32 * i;
-        gt[i] = nullptr;
-        if (rt < valid) {
-            if (DUAL) {
-                const int src = row_src[p0 + rt];
-                if (src >= 0 && src < n_src) gt[i] = act + static_cast<size_t>(src >> 1) * ld_act + 8 * c;
-            } else {
-                gt[i] = act + static_cast<size_t>(p0 + rt) * ld_act + 8 * c;
-            }
-        }
-    }
-
-    uint4 sw[8], st[8];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sw[i] = *reinterpret_cast<const uint4*>(gw[i] + k0);
-            st[i] = (gt[i] != nullptr) ? *reinterpret_cast<const uint4*>(gt[i] + k0) : zero4();
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = r0 + 32 * i;
-            lds_w[buf][row * 8 + swz(row, c)] = sw[i];
-            lds_t[buf][row * 8 + swz(row, c)] = st[i];
-        }
-    };
-
-    // ---- MFMA fragments: 4 weight blocks x 4 token blocks of 32x32 per wave
-    int wrow_blk[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (DUAL)
-            wrow_blk[j] = (j < 2 ? 0 : kTW / 2) + wave_w * 64 + (j & 1) * 32;
-        else
-            wrow_blk[j] = wave_w * 128 + j * 32;
-    }
-    const int trow0 = wave_t * 128;
-    // token blocks of this wave that hold at least one real row
-    const int nact = max(0, min(4, (valid - trow0 + 31) >> 5));
-
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
-
-    const int nk = Kdim / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    const int fr = lane & 31;
-    const int fk = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int ch = 2 * s + fk;
-            uint4 af[4], bfr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wrow_blk[j] + fr;
-                af[j] = lds_w[buf][row * 8 + swz(row, ch)];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = trow0 + i * 32 + fr;
-                bfr[i] = lds_t[buf][row * 8 + swz(row, ch)];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nact) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(af[j]), as_bf16x8(bfr[i]), acc[j][i], 0, 0, 0);
-                }
-            }
-        }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue.  32x32 C layout: lane l holds column (token) l%32 and rows
-    // (weight rows) 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = p0 + trow0 + i * 32 + fr;
-        if (p >= row_end) continue;
-        if (DUAL) {
-            bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
-            const int f0 = wt * (kTW / 2) + wave_w * 64;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int f = f0 + jj * 32 + 8 * q4 + 4 * fk;
-                    float v[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        v[u] = silu_f32(acc[jj][i][4 * q4 + u]) * acc[jj + 2][i][4 * q4 + u];
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(hrow + f) = o;
-                }
-            }
-        } else {
-            float* yrow = static_cast<float*>(out) + static_cast<size_t>(p) * ld_out;
-            const int j0 = wt * kTW + wave_w * 128;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int col = j0 + j * 32 + 8 * q4 + 4 * fk;
-                    f32x4_t v = {acc[j][i][4 * q4], acc[j][i][4 * q4 + 1], acc[j][i][4 * q4 + 2],
-                                 acc[j][i][4 * q4 + 3]};
-                    *reinterpret_cast<f32x4_t*>(yrow + col) = v;
-                }
-        }
-    }
-}
-
-// ===========================================================================
 // fp32 kernel (tile_m = 16)
 // ===========================================================================
 //
@@ -501,13 +312,7 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
                                                   static_cast<const bf16_t*>(w3), h, s.d, s.F, s.d,
                                                   s.T * s.K, pmax_rows(s, 16));
     } else {
-        const int n_tt = max_tiles(s, kTT);
-        const int n_wt = s.F / (kTW / 2);
-        const int G = (n_tt * n_wt + 7) / 8 * 8;
-        tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts,
-                                              offsets, static_cast<const bf16_t*>(w1),
-                                              static_cast<const bf16_t*>(w3), h, s.d, s.F, s.d,
-                                              n_tt, n_wt, s.F, s.T * s.K, pmax_rows(s, kTT));
+        return launch_tiled(s, true, x, row_src, counts, offsets, w1, w3, h, st);
     }
     return hipGetLastError();
 }
@@ -527,13 +332,7 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
                                                    y_perm, s.F, s.d, s.F, s.T * s.K,
                                                 pmax_rows(s, 16));
     } else {
-        const int n_tt = max_tiles(s, kTT);
-        const int n_wt = s.d / kTW;
-        const int G = (n_tt * n_wt + 7) / 8 * 8;
-        tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts,
-                                               offsets, static_cast<const bf16_t*>(w2), nullptr,
-                                               y_perm, s.F, s.d, s.F, n_tt, n_wt, s.d, s.T * s.K,
-                                               pmax_rows(s, kTT));
+        return launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st);
     }
     return hipGetLastError();
 }

@@ -71,6 +71,12 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
 hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
                        const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st);
 
+// LDS-tiled MFMA kernels (bf16, tile_m 256): gate_up selects SiLU(act.wa) * (act.wb)
+// into bf16 `out`, otherwise act.wa into fp32 `out`.
+hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
+                        const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
+                        void* out, hipStream_t st);
+
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
                           const float* gate, const void* residual, void* y, hipStream_t st);
 
