@@ -21,9 +21,12 @@
 //   * MFMA fragments are double-buffered in registers: the second k16 half of
 //     a stage and the first half of the next stage are read while the MFMAs of
 //     the previous half run.
-//   * LDS rows are 4 chunks of 16 bytes; chunk c of row r sits at c ^ g(r),
-//     g(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 32-row fragment reads hit
-//     distinct banks for both 128-byte and 256-byte bank windows.
+//   * LDS rows are 4 chunks of 16 bytes; chunk c of row r sits at c ^ g(r) with
+//     g(r) = (r2 ^ r3) | (r3 ^ r4) << 1 (bits of r).  gfx950's LDS has 64
+//     banks; a 32-row fragment read (ds_read_b128) is served in 16-lane phases
+//     (lanes 0-7 with 16-23, 8-15 with 24-31, measured with
+//     SQ_LDS_BANK_CONFLICT), and this g gives each phase all 64 banks, as it
+//     also does for 16 consecutive lanes.
 //   * Tile order: workgroup b runs on XCD b % 8; each XCD gets a contiguous run
 //     of tiles, enumerated as groups of GN weight tiles x all token tiles (token
 //     tiles of one expert are adjacent), so the ~32 tiles an XCD runs at once
@@ -48,7 +51,9 @@ constexpr int kDmaPerStage = 8;              // global_load_lds per lane per sta
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz(int row) {
+    return (((row >> 2) ^ (row >> 3)) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
+}
 
 __device__ __forceinline__ void dma16(const bf16_t* src, uint4* lds_wave_base) {
     // address-space conversions need C-style casts
@@ -114,14 +119,21 @@ __device__ __forceinline__ void read_frags(const TileCtx<DUAL>& c, const uint4* 
     for (int i = 0; i < 4; ++i) f.b[i] = p[c.tblk0 + i * 32 * kChunks];
 }
 
-__device__ __forceinline__ void mfma_16(const Frags& f, f32x16_t (&acc)[4][4]) {
+// MFMAs number q = LO .. HI-1 of the 16 of a k16 half (token block q/4, weight block q%4).
+template <int LO, int HI>
+__device__ __forceinline__ void mfma_range(const Frags& f, f32x16_t (&acc)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[j]), as_bf16x8(f.b[i]),
-                                                                acc[j][i], 0, 0, 0);
+    for (int q = LO; q < HI; ++q) {
+        const int i = q / 4, j = q % 4;
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[j]), as_bf16x8(f.b[i]),
+                                                            acc[j][i], 0, 0, 0);
+    }
 }
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
+constexpr int kSchedDsRead = 0x100;
 
 // One stage of the main loop: stage kt lives in `cur`, `nxt` holds stage kt+1
 // and `dma` receives stage kt+3.  LATER = stages issued after kt+1 that may
@@ -131,14 +143,42 @@ template <bool DUAL, bool ACTIVE, bool DMA, int LATER, bool NEXT>
 __device__ __forceinline__ void stage_step(const TileCtx<DUAL>& c, const uint4* __restrict__ cur,
                                            const uint4* __restrict__ nxt, uint4* __restrict__ dma,
                                            int kt, Frags& f0, Frags& f1, f32x16_t (&acc)[4][4]) {
+    if (!ACTIVE) {
+        if (DMA) issue_stage(c, dma, (kt + 3) * kBK);
+        if (NEXT) ring_barrier<LATER * kDmaPerStage>();
+        return;
+    }
+    // First k16 half: its 16 MFMAs carry the reads of the second half's
+    // fragments and the copies of stage kt+3, one between each pair of MFMAs.
     if (DMA) issue_stage(c, dma, (kt + 3) * kBK);
     read_frags(c, cur, 1, f1);
-    if (ACTIVE) mfma_16(f0, acc);
+    mfma_range<0, 16>(f0, acc);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (DMA) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // A few MFMAs of the second half stay in the pipe across the barrier.
+    mfma_range<0, 4>(f1, acc);
+    __builtin_amdgcn_sched_barrier(0);
     if (NEXT) {
         ring_barrier<LATER * kDmaPerStage>();
         read_frags(c, nxt, 0, f0);
     }
-    if (ACTIVE) mfma_16(f1, acc);
+    mfma_range<4, 16>(f1, acc);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (NEXT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // The K loop over nk stages (nk a multiple of 4, >= 4); stages 0..2 are
