@@ -142,7 +142,8 @@ moe_status_t moe_router_topk(const moe_layer_desc_t* desc, int32_t T, const void
     if (T == 0) return MOE_OK;
     if (x == nullptr || w_gate == nullptr || topk_idx == nullptr || topk_gate == nullptr)
         return MOE_ERR_INVALID_ARGUMENT;
-    if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_gate) || (logits_out != nullptr && !aligned16(logits_out)))
+        return MOE_ERR_INVALID_ARGUMENT;
     return hip_status(moe::launch_router_topk(shape_of(desc, T), x, w_gate, topk_idx, topk_gate,
                                               logits_out, static_cast<hipStream_t>(stream)));
 }

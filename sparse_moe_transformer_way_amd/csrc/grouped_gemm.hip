@@ -49,12 +49,14 @@ __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // ===========================================================================
 //
 // Block = 4 waves, one expert (blockIdx.y), one slab of kRB*16 weight rows
-// (blockIdx.x).  Wave w covers K range [w*K/4, (w+1)*K/4) in super-steps of 128:
-// lane (r = l%16, g = l/16) loads 64 contiguous bytes (k = base + 32g .. +32) of
-// weight row r of each 16-row block, and the same k range of activation row r of
-// each 16-row token block.  MFMA j (0..3) of a super-step takes elements
-// [8j, 8j+8) of both: the contraction pairs equal k on both sides, so this
-// permutation of k is exact.
+// (blockIdx.x).  Wave w covers K range [w*K/4, (w+1)*K/4) in super-steps of 128.
+// Load j (0..3) of a super-step gives lane (r = l%16, g = l/16) the 8 elements
+// k = base + 32j + 8g .. +8 of weight row r of a 16-row block, so one load
+// instruction reads 64 contiguous bytes of each of 16 rows (this streams at
+// ~5.9 TB/s on MI355X, against ~3.6 TB/s when each lane instead reads 64
+// contiguous bytes by itself).  The activation rows are loaded the same way and
+// MFMA j pairs load j of both operands: the contraction pairs equal k on both
+// sides, so this permutation of k is exact.
 //
 // DUAL (gate/up): row blocks 0,1 are w1 rows f0..f0+31, blocks 2,3 are w3 rows
 // f0..f0+31; the epilogue forms SiLU(a1) * a3.  Otherwise (down): 4 blocks of
@@ -93,13 +95,13 @@ __global__ __launch_bounds__(256) void stream_kernel(
 #pragma unroll
         for (int b = 0; b < kStreamRB; ++b) {
             const bf16_t* base = (b < 2) ? wa : wb;
-            wrow[b] = base + (static_cast<size_t>(e) * Nw + f0 + (b & 1) * 16 + r) * Kdim + 32 * g;
+            wrow[b] = base + (static_cast<size_t>(e) * Nw + f0 + (b & 1) * 16 + r) * Kdim + 8 * g;
         }
     } else {
         const int j0 = blockIdx.x * 64;
 #pragma unroll
         for (int b = 0; b < kStreamRB; ++b)
-            wrow[b] = wa + (static_cast<size_t>(e) * Nw + j0 + b * 16 + r) * Kdim + 32 * g;
+            wrow[b] = wa + (static_cast<size_t>(e) * Nw + j0 + b * 16 + r) * Kdim + 8 * g;
     }
 
     for (int tb0 = 0; tb0 < ntb; tb0 += kStreamMaxTB) {
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
             if (tb < ntp) {
                 if (DUAL) {
                     const int src = (p < seg + cnt) ? row_src[p] : -1;
-                    if (src >= 0 && src < n_src) arow[tb] = act + static_cast<size_t>(src >> 1) * ld_act + 32 * g;
+                    if (src >= 0 && src < n_src) arow[tb] = act + static_cast<size_t>(src >> 1) * ld_act + 8 * g;
                 } else if (p < seg + cnt) {
-                    arow[tb] = act + static_cast<size_t>(p) * ld_act + 32 * g;
+                    arow[tb] = act + static_cast<size_t>(p) * ld_act + 8 * g;
                 }
             }
         }
@@ -130,18 +132,17 @@ __global__ __launch_bounds__(256) void stream_kernel(
             u32x4_t wv[kStreamRB][4];
 #pragma unroll
             for (int b = 0; b < kStreamRB; ++b) {
-                const u32x4_t* p = reinterpret_cast<const u32x4_t*>(wrow[b] + k);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wv[b][j] = __builtin_nontemporal_load(p + j);
+                for (int j = 0; j < 4; ++j)
+                    wv[b][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wrow[b] + k + 32 * j));
             }
 #pragma unroll
             for (int tb = 0; tb < kStreamMaxTB; ++tb) {
                 if (tb < ntp) {
                     uint4 av[4];
                     if (arow[tb] != nullptr) {
-                        const uint4* p = reinterpret_cast<const uint4*>(arow[tb] + k);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) av[j] = p[j];
+                        for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(arow[tb] + k + 32 * j);
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) av[j] = zero4();

@@ -7,13 +7,15 @@
 // softmax).  Softmax of a vector whose other entries are -inf reduces to the
 // two-term form g0 = 1/(1+e), g1 = e/(1+e), e = exp(l_second - l_first).
 //
-// Layout: one wave handles TPW tokens.  Lane j covers the 8 consecutive
-// channels [8j + 512c, 8j + 512c + 8) of chunk c, so x loads are 16-byte (bf16)
-// or 32-byte (fp32) per lane and contiguous across the wave, and the matching
-// 8 rows of W_g (8 x 8 fp32 = 256 B) are contiguous per lane.  The 4 waves of a
-// block read the same W_g rows, which then come from L1/L2.  Per-lane partial
-// sums for the 8 experts are combined with an xor butterfly, so every lane ends
-// with the full logits and lane t finishes token t.
+// Layout: a block of 4 waves handles 8 tokens; the d channels are cut into
+// 8-channel chunks and wave w takes the w-th quarter of the chunks, so a token's
+// dot products are spread over 256 lanes (few sequential steps even at decode
+// batch sizes).  Lane j of a wave covers chunks j, j+64, ... of its quarter:
+// x loads are 16-byte (bf16) or 32-byte (fp32) per lane and contiguous across
+// the wave, and the matching 8 rows of W_g (8 x 8 fp32 = 256 B) are contiguous
+// per lane.  Per-lane partial sums go through an xor butterfly inside the wave,
+// then the 4 wave sums are added in wave order through LDS (a fixed order, so
+// the logits are deterministic), and lane t of wave 0 finishes token t.
 #include "moe_common.h"
 
 namespace moe {
@@ -21,9 +23,8 @@ namespace moe {
 namespace {
 
 constexpr int kExperts = 8;
-constexpr int kTPW = 4;           // tokens per wave
-constexpr int kWaves = 4;         // waves per block
-constexpr int kTokPerBlock = kTPW * kWaves;
+constexpr int kTok = 8;           // tokens per block
+constexpr int kWaves = 4;         // waves per block, splitting d
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ xv,
@@ -31,18 +32,22 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
                                                           int d, int32_t* __restrict__ idx,
                                                           float* __restrict__ gate,
                                                           float* __restrict__ logits) {
+    __shared__ float part[kWaves][kTok][kExperts];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = (blockIdx.x * kWaves + wave) * kTPW;
-    if (t0 >= T) return;
+    const int t0 = blockIdx.x * kTok;
+    const int nch = d >> 3;
+    const int cbeg = wave * nch / kWaves;
+    const int cend = (wave + 1) * nch / kWaves;
 
-    float acc[kTPW][kExperts];
+    float acc[kTok][kExperts];
 #pragma unroll
-    for (int t = 0; t < kTPW; ++t)
+    for (int t = 0; t < kTok; ++t)
 #pragma unroll
         for (int e = 0; e < kExperts; ++e) acc[t][e] = 0.0f;
 
-    for (int k0 = lane * 8; k0 < d; k0 += 512) {
+    for (int ch = cbeg + lane; ch < cend; ch += 64) {
+        const int k0 = ch * 8;
         float w[8][kExperts];
         const float4* wp = reinterpret_cast<const float4*>(wg + static_cast<size_t>(k0) * kExperts);
 #pragma unroll
@@ -52,7 +57,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
             w[j][4] = b.x; w[j][5] = b.y; w[j][6] = b.z; w[j][7] = b.w;
         }
 #pragma unroll
-        for (int t = 0; t < kTPW; ++t) {
+        for (int t = 0; t < kTok; ++t) {
             if (t0 + t < T) {
                 float xf[8];
                 if (BF16) {
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
     }
 
 #pragma unroll
-    for (int t = 0; t < kTPW; ++t)
+    for (int t = 0; t < kTok; ++t)
 #pragma unroll
         for (int e = 0; e < kExperts; ++e) {
             float v = acc[t][e];
@@ -82,37 +87,44 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
             acc[t][e] = v;
         }
-
+    if (lane == 0) {
 #pragma unroll
-    for (int t = 0; t < kTPW; ++t) {
-        const int tok = t0 + t;
-        if (lane == t && tok < T) {
-            // Order key (logit descending, index ascending): strict '>' keeps the
-            // earlier (lower) index on equality.
-            int i0 = 0, i1 = -1;
-            float v0 = acc[t][0], v1 = -INFINITY;
+        for (int t = 0; t < kTok; ++t)
 #pragma unroll
-            for (int e = 1; e < kExperts; ++e) {
-                const float v = acc[t][e];
-                if (v > v0) {
-                    i1 = i0; v1 = v0; i0 = e; v0 = v;
-                } else if (v > v1 || i1 < 0) {
-                    i1 = e; v1 = v;
-                }
-            }
-            const float ex = expf(v1 - v0);
-            const float s = 1.0f + ex;
-            idx[2 * tok] = i0;
-            idx[2 * tok + 1] = i1;
-            gate[2 * tok] = 1.0f / s;
-            gate[2 * tok + 1] = ex / s;
+            for (int e = 0; e < kExperts; ++e) part[wave][t][e] = acc[t][e];
+    }
+    __syncthreads();
+    if (wave != 0 || lane >= kTok) return;
+    const int t = lane;
+    const int tok = t0 + t;
+    if (tok >= T) return;
+    float l[kExperts];
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e)
+        l[e] = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
+    // Order key (logit descending, index ascending): strict '>' keeps the
+    // earlier (lower) index on equality.
+    int i0 = 0, i1 = -1;
+    float v0 = l[0], v1 = -INFINITY;
+#pragma unroll
+    for (int e = 1; e < kExperts; ++e) {
+        const float v = l[e];
+        if (v > v0) {
+            i1 = i0; v1 = v0; i0 = e; v0 = v;
+        } else if (v > v1 || i1 < 0) {
+            i1 = e; v1 = v;
         }
-        if (logits != nullptr && lane < kExperts && tok < T) {
-            float v = acc[t][0];
-#pragma unroll
-            for (int e = 1; e < kExperts; ++e) v = (lane == e) ? acc[t][e] : v;
-            logits[static_cast<size_t>(tok) * kExperts + lane] = v;
-        }
+    }
+    const float ex = expf(v1 - v0);
+    const float sum = 1.0f + ex;
+    idx[2 * tok] = i0;
+    idx[2 * tok + 1] = i1;
+    gate[2 * tok] = 1.0f / sum;
+    gate[2 * tok + 1] = ex / sum;
+    if (logits != nullptr) {
+        float4* lp = reinterpret_cast<float4*>(logits + static_cast<size_t>(tok) * kExperts);
+        lp[0] = make_float4(l[0], l[1], l[2], l[3]);
+        lp[1] = make_float4(l[4], l[5], l[6], l[7]);
     }
 }
 
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
 
 hipError_t launch_router_topk(const Shape& s, const void* x, const float* wg, int32_t* idx,
                               float* gate, float* logits, hipStream_t st) {
-    const int blocks = (s.T + kTokPerBlock - 1) / kTokPerBlock;
+    const int blocks = (s.T + kTok - 1) / kTok;
     if (s.bf16)
         router_topk_kernel<true><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
     else
