@@ -54,11 +54,12 @@ long long pmax(const moe_layer_desc_t* d, int32_t T, int32_t tile_m) {
     return static_cast<long long>(T) * d->top_k + static_cast<long long>(d->n_experts) * (tile_m - 1);
 }
 
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
 moe::Shape shape_of(const moe_layer_desc_t* d, int32_t T) {
     return moe::Shape{T, d->d_model, d->d_ffn, d->n_experts, d->top_k, d->act_dtype == MOE_BF16};
 }
-
-moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Workspace carving of moe_layer_forward.
 struct LayerWs {
@@ -70,6 +71,7 @@ struct LayerWs {
     int32_t* row_of;
     void* h;
     float* y_perm;
+    float* y_perm_hi;  // second K-partial of the down projection, or nullptr
     size_t bytes;
 };
 
@@ -90,7 +92,10 @@ LayerWs carve_layer(const moe_layer_desc_t* d, int32_t T, int32_t tile_m, char* 
     w.row_src = reinterpret_cast<int32_t*>(take(P * 4));
     w.row_of = reinterpret_cast<int32_t*>(take(TK * 4));
     w.h = take(P * static_cast<size_t>(d->d_ffn) * dtype_size(d->act_dtype));
-    w.y_perm = reinterpret_cast<float*>(take(P * static_cast<size_t>(d->d_model) * 4));
+    // the tiled down projection may write two K-partial sums back to back
+    const int parts = (tile_m == 256) ? moe::tiled_down_ksplit(shape_of(d, T)) : 1;
+    w.y_perm = reinterpret_cast<float*>(take(parts * P * static_cast<size_t>(d->d_model) * 4));
+    w.y_perm_hi = parts == 2 && base != nullptr ? w.y_perm + P * static_cast<size_t>(d->d_model) : nullptr;
     w.bytes = off;
     return w;
 }
@@ -269,9 +274,12 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
         return MOE_ERR_HIP;
     if ((e = moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, w1, w3, w.h, st)) != hipSuccess)
         return MOE_ERR_HIP;
-    if ((e = moe::launch_down(sh, tile_m, w.h, counts, w.offsets, w2, w.y_perm, st)) != hipSuccess)
+    int parts = 1;
+    if ((e = moe::launch_down(sh, tile_m, w.h, counts, w.offsets, w2, w.y_perm, st, w.y_perm_hi, &parts)) !=
+        hipSuccess)
         return MOE_ERR_HIP;
-    if ((e = moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st)) != hipSuccess)
+    if ((e = moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st,
+                                 parts == 2 ? w.y_perm_hi : nullptr)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

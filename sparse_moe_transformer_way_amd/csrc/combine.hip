@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ residual, void* y,
-                                                      int d) {
+                                                      int d, const float* __restrict__ y_perm_hi) {
     const int t = blockIdx.x;
     const int r0 = row_of[2 * t], r1 = row_of[2 * t + 1];
     const float g0 = gate[2 * t], g1 = gate[2 * t + 1];
@@ -29,11 +29,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (r0 >= 0) {
-            const float4 a = p0[c];
+            float4 a = p0[c];
+            if (y_perm_hi != nullptr) {
+                const float4 a2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r0) * d)[c];
+                a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+            }
             v[0] = g0 * a.x; v[1] = g0 * a.y; v[2] = g0 * a.z; v[3] = g0 * a.w;
         }
         if (r1 >= 0) {
-            const float4 b = p1[c];
+            float4 b = p1[c];
+            if (y_perm_hi != nullptr) {
+                const float4 b2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r1) * d)[c];
+                b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+            }
             v[0] += g1 * b.x; v[1] += g1 * b.y; v[2] += g1 * b.z; v[3] += g1 * b.w;
         }
         const size_t o = static_cast<size_t>(t) * d + 4 * c;
@@ -105,11 +113,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
 }  // namespace
 
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
-                          const float* gate, const void* residual, void* y, hipStream_t st) {
+                          const float* gate, const void* residual, void* y, hipStream_t st,
+                          const float* y_perm_hi) {
     if (s.bf16)
-        combine_kernel<true><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d);
+        combine_kernel<true><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi);
     else
-        combine_kernel<false><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d);
+        combine_kernel<false><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi);
     return hipGetLastError();
 }
 

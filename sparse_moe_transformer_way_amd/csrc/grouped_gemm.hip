@@ -319,7 +319,9 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
 }
 
 hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
-                       const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st) {
+                       const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
+                       float* y_perm_hi, int* n_parts) {
+    if (n_parts != nullptr) *n_parts = 1;
     if (!s.bf16) {
         dim3 grid(max_tiles(s, 16), (s.d + 63) / 64);
         f32_kernel<false><<<grid, 256, 0, st>>>(static_cast<const float*>(h), nullptr, counts,
@@ -333,7 +335,15 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
                                                    y_perm, s.F, s.d, s.F, s.T * s.K,
                                                 pmax_rows(s, 16));
     } else {
-        return launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st);
+        int ks = 1;
+        if (y_perm_hi != nullptr) {
+            ks = tiled_down_ksplit(s);
+            // the second part lands one P x d block after y_perm
+            const size_t P = static_cast<size_t>(pmax_rows(s, 256));
+            if (ks == 2 && y_perm_hi != y_perm + P * s.d) ks = 1;
+        }
+        if (n_parts != nullptr) *n_parts = ks;
+        return launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks);
     }
     return hipGetLastError();
 }

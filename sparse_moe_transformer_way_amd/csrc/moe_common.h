@@ -68,17 +68,26 @@ hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_
 hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32_t* row_src,
                           const int32_t* counts, const int32_t* offsets, const void* w1,
                           const void* w3, void* h, hipStream_t st);
+// With y_perm_hi != nullptr (tile_m 256 only) the K range may be cut in two:
+// the returned count of partial buffers (1 or 2) tells the caller whether
+// y_perm_hi was written; y = y_perm + y_perm_hi then.
 hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
-                       const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st);
+                       const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
+                       float* y_perm_hi = nullptr, int* n_parts = nullptr);
+
+// Number of K parts the tiled down projection uses when allowed to split.
+int tiled_down_ksplit(const Shape& s);
 
 // LDS-tiled MFMA kernels (bf16, tile_m 256): gate_up selects SiLU(act.wa) * (act.wb)
 // into bf16 `out`, otherwise act.wa into fp32 `out`.
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
-                        void* out, hipStream_t st);
+                        void* out, hipStream_t st, int ksplit = 1);
 
+// y_perm_hi (optional): second partial sum of the down projection, added to y_perm.
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
-                          const float* gate, const void* residual, void* y, hipStream_t st);
+                          const float* gate, const void* residual, void* y, hipStream_t st,
+                          const float* y_perm_hi = nullptr);
 
 hipError_t launch_rmsnorm(int T, int d, bool bf16, const void* h, float eps, void* x_out,
                           hipStream_t st);

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_tt, int n_wt, int GN,
-    int ld_out, int n_src, int P) {
+    int ld_out, int n_src, int P, int ksplit, size_t split_stride) {
     __shared__ uint4 st0[kStageVec];
     __shared__ uint4 st1[kStageVec];
     __shared__ uint4 st2[kStageVec];
@@ -217,8 +217,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- tile of this workgroup
     const int nblk = gridDim.x;  // a multiple of 8
-    const int L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    if (L >= n_tt * n_wt) return;
+    const int L_all = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    // K may be cut into `ksplit` parts; part s adds over k in [s*K/ksplit,
+    // (s+1)*K/ksplit) and writes its own output buffer (out + s*split_stride).
+    const int split = L_all / (n_tt * n_wt);
+    const int L = L_all - split * (n_tt * n_wt);
+    if (split >= ksplit) return;
+    const int kpart = Kdim / ksplit;
+    const int kbase = split * kpart;
+    out = static_cast<char*>(out) + split * split_stride * (DUAL ? sizeof(bf16_t) : sizeof(float));
     const int per_group = n_tt * GN;
     const int grp = L / per_group;
     const int rem = L - grp * per_group;
@@ -252,15 +259,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (DUAL) {
                 const int f0 = wt * (kTW / 2);
                 const bf16_t* base = (r < kTW / 2) ? wa : wb;
-                c.gw[j] = base + (static_cast<size_t>(e) * Nw + f0 + (r & (kTW / 2 - 1))) * Kdim + 8 * chunk;
+                c.gw[j] = base + (static_cast<size_t>(e) * Nw + f0 + (r & (kTW / 2 - 1))) * Kdim + kbase + 8 * chunk;
                 int src = (r < valid) ? row_src[p0 + r] : first_src;
                 if (src < 0 || src >= n_src) src = first_src;
                 if (src < 0 || src >= n_src) src = 0;
-                c.gt[j] = act + static_cast<size_t>(src >> 1) * ld_act + 8 * chunk;
+                c.gt[j] = act + static_cast<size_t>(src >> 1) * ld_act + kbase + 8 * chunk;
             } else {
-                c.gw[j] = wa + (static_cast<size_t>(e) * Nw + wt * kTW + r) * Kdim + 8 * chunk;
+                c.gw[j] = wa + (static_cast<size_t>(e) * Nw + wt * kTW + r) * Kdim + kbase + 8 * chunk;
                 const int pr = (r < valid) ? p0 + r : p0;
-                c.gt[j] = act + static_cast<size_t>(pr) * ld_act + 8 * chunk;
+                c.gt[j] = act + static_cast<size_t>(pr) * ld_act + kbase + 8 * chunk;
             }
         }
         c.dma_w = (wave * 64) * kChunks;
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
 
-    const int nk = Kdim / kBK;  // a multiple of 4
+    const int nk = kpart / kBK;  // a multiple of 4
     issue_stage(c, st0, 0);
     issue_stage(c, st1, kBK);
     issue_stage(c, st2, 2 * kBK);
@@ -346,22 +353,33 @@ int group_size(int n_wt) {
 
 }  // namespace
 
+int tiled_down_ksplit(const Shape& s) {
+    // Cut the down projection's K in two when its tiles would not fill four
+    // rounds of the 256 CUs (the last, partly empty round then costs less).
+    const int P = s.T * s.K + s.n * (kTT - 1);
+    const int n_tt = (P + kTT - 1) / kTT;
+    const int n_wt = s.d / kTW;
+    return (n_tt * n_wt < 4 * 256 && (s.F / 2) % (4 * kBK) == 0) ? 2 : 1;
+}
+
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
-                        void* out, hipStream_t st) {
+                        void* out, hipStream_t st, int ksplit) {
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = gate_up ? s.F / (kTW / 2) : s.d / kTW;
     const int GN = group_size(n_wt);
-    const int G = (n_tt * n_wt + 7) / 8 * 8;
+    const int G = (n_tt * n_wt * ksplit + 7) / 8 * 8;
+    const size_t split_stride = static_cast<size_t>(P) * (gate_up ? s.F : s.d);
     if (gate_up)
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
                                               static_cast<const bf16_t*>(wa), static_cast<const bf16_t*>(wb),
-                                              out, s.d, s.F, s.d, n_tt, n_wt, GN, s.F, s.T * s.K, P);
+                                              out, s.d, s.F, s.d, n_tt, n_wt, GN, s.F, s.T * s.K, P,
+                                              ksplit, split_stride);
     else
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
-                                               n_tt, n_wt, GN, s.d, s.T * s.K, P);
+                                               n_tt, n_wt, GN, s.d, s.T * s.K, P, ksplit, split_stride);
     return hipGetLastError();
 }
 
