@@ -31,7 +31,10 @@ WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3}
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_way_amd", "csrc", "grouped_gemm.hip")
+CSRC = os.path.join(ROOT, "sparse_moe_transformer_way_amd", "csrc")
+# source file of each kernel the roofline can name
+KERNEL_SRC = {"gate_up_stream": "grouped_gemm.hip", "gate_up_tiled": "tiled_gemm.hip",
+              "gate_up_f32": "grouped_gemm.hip"}
 
 
 def parse_args():
@@ -57,12 +60,12 @@ def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter
     summary, or None when there is none or the kernel source changed since."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.md")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SRC:
         return None
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or not h or h.group(1) != source_digest(GEMM_SRC):
+    if not m or not h or h.group(1) != source_digest(os.path.join(CSRC, KERNEL_SRC[kernel])):
         return None
     return float(m.group(1))
 
