@@ -1,6 +1,6 @@
 """ctypes loading of libmoe_mi355x.so and the C declarations of include/moe.h.
 
-The library must have been built (python -m sparse_moe_transformer_way_amd.build);
+The library must have been built (python sparse_moe_transformer_way_amd/build.py);
 there is no fallback of any kind: a missing library raises at import.
 """
 from __future__ import annotations
@@ -62,7 +62,7 @@ SIGNATURES = {
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m sparse_moe_transformer_way_amd.build` "
+            f"{path} is missing: build it with `python sparse_moe_transformer_way_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():

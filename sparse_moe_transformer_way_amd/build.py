@@ -1,6 +1,9 @@
 """Build libmoe_mi355x.so for gfx950 from csrc/*.hip with hipcc.
 
-    python -m sparse_moe_transformer_way_amd.build
+    python sparse_moe_transformer_way_amd/build.py
+
+(run as a file: importing the package loads the library, which is what this
+script builds).  Only the standard library is used.
 
 Objects go to sparse_moe_transformer_way_amd/_build/, the shared library next
 to this file.  Every call recompiles everything (a few seconds per file).
@@ -58,7 +61,8 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol fails the link instead of the first load
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
