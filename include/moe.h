@@ -74,7 +74,8 @@ int32_t moe_version(void);
 
 /* Padding granularity of the permuted layout that moe_layer_forward uses for T
  * tokens: 16 for fp32 and for bf16 with T <= 64 (weight-streaming kernels),
- * 256 for larger bf16 batches (LDS-tiled MFMA kernels).  Returns 0 if the
+ * 256 for larger bf16 batches (LDS-tiled MFMA kernels) while tile_m 256 is
+ * supported for T (see moe_expert_gate_up), else 16.  Returns 0 if the
  * descriptor is invalid or unsupported. */
 int32_t moe_default_tile_m(const moe_layer_desc_t* desc, int32_t T);
 
@@ -133,7 +134,8 @@ moe_status_t moe_permute(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m
  * counts/offsets/row_src are moe_permute's outputs for the same tile_m.
  * tile_m == 16 selects weight-streaming kernels (suited to few rows per
  * expert; correct for any count), tile_m == 256 selects the LDS-tiled MFMA
- * kernels (bf16 only).
+ * kernels (bf16 only, and only while T * d_model * 2 bytes stay below 4 GiB;
+ * beyond that every call taking tile_m 256 returns MOE_ERR_UNSUPPORTED).
  */
 moe_status_t moe_expert_gate_up(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m,
                                 const void* x, const int32_t* row_src, const int32_t* counts,

@@ -39,14 +39,19 @@ moe_status_t check_T(int32_t T, const moe_layer_desc_t* d) {
     return MOE_OK;
 }
 
-int default_tile(const moe_layer_desc_t* d, int32_t T) {
-    if (d->act_dtype != MOE_BF16) return 16;
-    return T <= 64 ? 16 : 256;
+moe::Shape shape_of(const moe_layer_desc_t* d, int32_t T) {
+    return moe::Shape{T, d->d_model, d->d_ffn, d->n_experts, d->top_k, d->act_dtype == MOE_BF16};
 }
 
-moe_status_t check_tile(const moe_layer_desc_t* d, int32_t tile_m) {
+int default_tile(const moe_layer_desc_t* d, int32_t T) {
+    if (d->act_dtype != MOE_BF16) return 16;
+    return (T <= 64 || !moe::tiled_fits(shape_of(d, T))) ? 16 : 256;
+}
+
+moe_status_t check_tile(const moe_layer_desc_t* d, int32_t T, int32_t tile_m) {
     if (tile_m == 16) return MOE_OK;
-    if (tile_m == 256) return d->act_dtype == MOE_BF16 ? MOE_OK : MOE_ERR_UNSUPPORTED;
+    if (tile_m == 256)
+        return (d->act_dtype == MOE_BF16 && moe::tiled_fits(shape_of(d, T))) ? MOE_OK : MOE_ERR_UNSUPPORTED;
     return MOE_ERR_INVALID_ARGUMENT;
 }
 
@@ -57,9 +62,6 @@ long long pmax(const moe_layer_desc_t* d, int32_t T, int32_t tile_m) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-moe::Shape shape_of(const moe_layer_desc_t* d, int32_t T) {
-    return moe::Shape{T, d->d_model, d->d_ffn, d->n_experts, d->top_k, d->act_dtype == MOE_BF16};
-}
 
 // Workspace carving of moe_layer_forward.
 struct LayerWs {
@@ -127,14 +129,14 @@ int32_t moe_default_tile_m(const moe_layer_desc_t* desc, int32_t T) {
 int64_t moe_max_permuted_rows(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m) {
     if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return -1;
     if (tile_m == 0) tile_m = default_tile(desc, T);
-    if (check_tile(desc, tile_m) != MOE_OK) return -1;
+    if (check_tile(desc, T, tile_m) != MOE_OK) return -1;
     return pmax(desc, T, tile_m);
 }
 
 size_t moe_workspace_size(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m) {
     if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return 0;
     if (tile_m == 0) tile_m = default_tile(desc, T);
-    if (check_tile(desc, tile_m) != MOE_OK) return 0;
+    if (check_tile(desc, T, tile_m) != MOE_OK) return 0;
     return carve_layer(desc, T, tile_m, nullptr).bytes;
 }
 
@@ -159,7 +161,7 @@ moe_status_t moe_permute(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (counts == nullptr || offsets == nullptr || row_src == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     if (T > 0 && (topk_idx == nullptr || row_of == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
     // T == 0 still writes counts = 0, offsets = 0 and the all-padding row_src.
@@ -174,7 +176,7 @@ moe_status_t moe_expert_gate_up(const moe_layer_desc_t* desc, int32_t T, int32_t
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
     if (x == nullptr || row_src == nullptr || counts == nullptr || offsets == nullptr ||
         w1 == nullptr || w3 == nullptr || h == nullptr)
@@ -191,7 +193,7 @@ moe_status_t moe_expert_down(const moe_layer_desc_t* desc, int32_t T, int32_t ti
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
     if (h == nullptr || counts == nullptr || offsets == nullptr || w2 == nullptr || y_perm == nullptr)
         return MOE_ERR_INVALID_ARGUMENT;
@@ -207,7 +209,7 @@ moe_status_t moe_grouped_swiglu(const moe_layer_desc_t* desc, int32_t T, int32_t
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if ((s = check_tile(desc, tile_m)) != MOE_OK) return s;
+    if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
     if (w2 == nullptr || y_perm == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     s = moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, h, stream);

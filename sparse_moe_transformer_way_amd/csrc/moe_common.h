@@ -75,6 +75,10 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
                        const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
                        float* y_perm_hi = nullptr, int* n_parts = nullptr);
 
+// Whether the tiled kernels can address this shape's token rows (gate/up
+// reaches the rows of x through 32-bit byte offsets: T * d_model * 2 bytes
+// must stay below 4 GiB).
+bool tiled_fits(const Shape& s);
 // Number of K parts the tiled down projection uses when allowed to split.
 int tiled_down_ksplit(const Shape& s);
 

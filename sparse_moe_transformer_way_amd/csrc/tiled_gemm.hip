@@ -13,27 +13,42 @@
 //     SiLU gate is formed in registers.  Each wave owns 128 x 128 outputs as
 //     4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane,
 //     kept in AGPRs; one wave per SIMD).
-//   * K advances 32 per stage.  A stage is 256 weight rows + 256 token rows of
-//     64 bytes = 32 KB, copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no
-//     register staging).  Four stage buffers form a ring with three stages in
-//     flight; the loop is unrolled by four so that every copy and every LDS
-//     read names one fixed buffer.  One barrier per stage.
-//   * MFMA fragments are double-buffered in registers: the second k16 half of
-//     a stage and the first half of the next stage are read while the MFMAs of
-//     the previous half run.
-//   * LDS rows are 4 chunks of 16 bytes; chunk c of row r sits at c ^ g(r) with
-//     g(r) = (r2 ^ r3) | (r3 ^ r4) << 1 (bits of r).  gfx950's LDS has 64
-//     banks; a 32-row fragment read (ds_read_b128) is served in 16-lane phases
-//     (lanes 0-7 with 16-23, 8-15 with 24-31, measured with
-//     SQ_LDS_BANK_CONFLICT), and this g gives each phase all 64 banks, as it
-//     also does for 16 consecutive lanes.
-//   * Tile order: workgroup b runs on XCD b % 8; each XCD gets a contiguous run
-//     of tiles, enumerated as groups of GN weight tiles x all token tiles (token
-//     tiles of one expert are adjacent), so the ~32 tiles an XCD runs at once
-//     share a few weight tiles and a few token tiles in its L2.
-//   * Padding rows of a token tile copy a real row (the copy cannot write
-//     zeros); their outputs are masked in the epilogue.  A wave whose 128 token
-//     rows are all padding skips its MFMAs.
+//   * K advances 64 per LDS buffer ("block").  A block is 256 weight rows +
+//     256 token rows of 128 bytes = 64 KB, copied HBM/L2 -> LDS by buffer loads
+//     with the LDS destination bit (no register staging), 8 rows x 128 bytes
+//     per wave instruction, so every request covers a whole 128-byte line
+//     (measured on MI355X: half-line copies of 32-k stages issued twice the L2
+//     requests and ran the kernels 8-11% slower).  Two buffers: block kb+2 is
+//     copied while block kb+1 lands and block kb is consumed.
+//   * A block is consumed as two 32-k stages of 32 MFMAs; each stage's 16
+//     fragments are read into a second register set under the previous
+//     stage's MFMAs, one read per two MFMAs, and the copies of a block are
+//     spread over its second stage the same way.  One barrier per block, before
+//     its second stage: it waits for block kb+1's copies and for every wave's
+//     reads of block kb, so block kb+2 may then be copied over it.  (Measured:
+//     bursts of fragment reads just ahead of their MFMAs left the matrix cores
+//     a third idle; this spacing keeps them busy.)
+//   * Copies address a wave-uniform buffer resource plus a 32-bit per-lane
+//     offset, with the k of the block (and the row group) as the scalar offset.
+//   * LDS rows are 8 chunks of 16 bytes; chunk c of row r sits at c ^ g(r) with
+//     g(r) = r1 | r2 << 1 | r4 << 2 (bits of r).  gfx950's LDS has 64 banks; a
+//     32-row fragment read (ds_read_b128) is served in 16-lane phases (lanes
+//     0-7 with 16-23, 8-15 with 24-31, measured with SQ_LDS_BANK_CONFLICT);
+//     in each phase the 8 even rows and the 8 odd rows get 8 distinct chunks,
+//     so the phase covers all 64 banks.  The copies write whole 1 KB runs.
+//   * Tile order: workgroup b runs on XCD b % 8, and each XCD gets a contiguous
+//     run of an expert-major enumeration (computed on the device from the
+//     segment offsets): expert by expert, groups of G weight tiles x all of the
+//     expert's token tiles, G ~ 32 / (the expert's token tiles).  The ~32 tiles
+//     an XCD runs at once (32 CUs) then read the same few weight and token
+//     tiles, so each k-slice comes from HBM once and from its L2 after that.
+//     (Measured on MI355X: with every tile's data L2-resident the kernels ran
+//     16% (gate/up) and 35% (down) faster than with an order that let a round
+//     straddle two experts.)
+//   * Padding rows of a token tile copy a real row (gate/up) or the padded rows
+//     of h (down); their outputs are masked in the epilogue.
+//   * K may be cut into two parts (down projection with few tiles): part s
+//     covers k in [s*K/2, (s+1)*K/2) and writes its own fp32 output buffer.
 #include "moe_common.h"
 
 namespace moe {
@@ -43,164 +58,158 @@ namespace {
 constexpr int kExperts = 8;
 constexpr int kTW = 256;                     // weight rows per tile
 constexpr int kTT = 256;                     // token rows per tile
-constexpr int kBK = 32;                      // k per stage
-constexpr int kChunks = kBK / 8;             // 16-byte chunks per LDS row
-constexpr int kStageVec = (kTW + kTT) * kChunks;  // uint4 per stage (32 KB)
-constexpr int kDmaPerStage = 8;              // global_load_lds per lane per stage
+constexpr int kBK = 64;                      // k per LDS buffer (one "block")
+constexpr int kChunks = kBK / 8;             // 16-byte chunks per LDS row (128-byte rows)
+constexpr int kBufVec = (kTW + kTT) * kChunks;  // uint4 per buffer (64 KB)
+constexpr int kCopies = 16;                  // copies per lane per block
+constexpr int kGroupVec = 8 * kChunks;       // uint4 of one 8-row copy group (1 KB)
+constexpr int kXcdTiles = 32;                // tiles an XCD runs at once (its CUs)
 
-typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
-__device__ __forceinline__ int swz(int row) {
-    return (((row >> 2) ^ (row >> 3)) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1);
+// g(r) = r1 | r2 << 1 | r4 << 2
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
+
+// Buffer resource over [base, base + 4 GiB); every offset the kernel adds is
+// in range by construction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting of gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
 }
 
-__device__ __forceinline__ void dma16(const bf16_t* src, uint4* lds_wave_base) {
-    // address-space conversions need C-style casts
-    __builtin_amdgcn_global_load_lds((gptr_t)(src), (lptr_t)(lds_wave_base), 16, 0, 0);
-}
-
-// s_waitcnt immediate (gfx9 encoding): at most N vector-memory operations of
-// this wave outstanding and none of its LDS reads (lgkmcnt 0); export count not
-// waited on.
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-
-// Workgroup barrier for the stage ring.  __syncthreads() carries a release
-// fence that waits for every outstanding copy into LDS (vmcnt 0), which would
-// drain the ring; here the caller waits for exactly the stage it needs, and the
-// empty asm statements only stop the compiler from moving memory accesses
-// across the barrier.
+// Workgroup barrier: waits until at most N of this wave's vector-memory
+// operations are outstanding and all its LDS reads are done.  The empty asm
+// statements only stop the compiler from moving memory accesses across it.
 template <int N>
-__device__ __forceinline__ void ring_barrier() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int p) {
-    int e = 0;
-#pragma unroll
-    for (int j = 1; j < kExperts; ++j) e = (p >= offsets[j]) ? j : e;
-    return e;
-}
+typedef u32x4_t Frag16[16];  // one 32-k stage's fragments: [k16 half][4 weight blocks, 4 token blocks]
 
-struct Frags {
-    uint4 a[4];  // weight blocks
-    uint4 b[4];  // token blocks
-};
-
-template <bool DUAL>
 struct TileCtx {
-    const bf16_t* gw[4];  // this lane's 4 weight source rows (+ chunk offset)
-    const bf16_t* gt[4];  // this lane's 4 token source rows (+ chunk offset)
-    int dma_w;            // uint4 offset of this wave's first weight DMA block in a stage
-    int dma_t;            // uint4 offset of this wave's first token DMA block in a stage
-    int rd[2];            // per-lane uint4 offset of its fragment row/chunk, k16 half 0 / 1
-    int wblk[4];          // weight block base rows (uint4 units, = row * kChunks)
-    int tblk0;            // token block base (uint4 units)
+    __amdgpu_buffer_rsrc_t wres;  // this wave's 64 weight rows (k origin at the part's start)
+    __amdgpu_buffer_rsrc_t tres;  // gate/up: x; down: this wave's 64 rows of h
+    uint32_t wo[2];               // lane byte offsets into the weight rows, groups j with bit 1 clear / set
+    uint32_t to[8];               // gate/up: lane byte offsets of its 8 token rows; down: to[0..1] like wo
+    int wstride;                  // bytes between 8-row weight groups
+    int tstride;                  // down: bytes between 8-row token groups; 0 for gate/up
+    int dma;                      // uint4 offset of this wave's first copy group in a buffer
+    int rd[4];                    // per (half of the block, k16 half): fragment index in weight block 0
+    int rdt;                      // uint4 distance from weight block 0 to token block 0
 };
 
+// Weight block j of this wave (uint4 offset from block 0).  Gate/up: blocks 0,
+// 1 are w1 rows, 2, 3 the same rows of w3 (LDS rows 128 on).
 template <bool DUAL>
-__device__ __forceinline__ void issue_stage(const TileCtx<DUAL>& c, uint4* __restrict__ buf, int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(c.gw[j] + k0, buf + c.dma_w + j * 16 * kChunks);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(c.gt[j] + k0, buf + c.dma_t + j * 16 * kChunks);
+__device__ __forceinline__ constexpr int wblk(int j) {
+    return (DUAL ? ((j < 2 ? 0 : kTW / 2) + (j & 1) * 32) : j * 32) * kChunks;
 }
 
+// Copy j (0-7 weights, 8-15 tokens) of a block: one wave instruction fills
+// one 8-row group (1 KB) of LDS, lane l at byte 16*l of it (row l/8).
 template <bool DUAL>
-__device__ __forceinline__ void read_frags(const TileCtx<DUAL>& c, const uint4* __restrict__ buf, int half,
-                                           Frags& f) {
-    const uint4* p = buf + c.rd[half];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.a[j] = p[c.wblk[j]];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.b[i] = p[c.tblk0 + i * 32 * kChunks];
-}
-
-// MFMAs number q = LO .. HI-1 of the 16 of a k16 half (token block q/4, weight block q%4).
-template <int LO, int HI>
-__device__ __forceinline__ void mfma_range(const Frags& f, f32x16_t (&acc)[4][4]) {
-#pragma unroll
-    for (int q = LO; q < HI; ++q) {
-        const int i = q / 4, j = q % 4;
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[j]), as_bf16x8(f.b[i]),
-                                                            acc[j][i], 0, 0, 0);
+__device__ __forceinline__ void copy_one(const TileCtx& c, uint4* __restrict__ buf, int k0, int j) {
+    // address-space conversion needs a C-style cast
+    if (j < 8) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.wres, (lptr_t)(buf + c.dma + j * kGroupVec), 16,
+                                                 c.wo[(j >> 1) & 1], j * c.wstride + 2 * k0, 0, 0);
+    } else {
+        const int jj = j - 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.tres, (lptr_t)(buf + kTW * kChunks + c.dma + jj * kGroupVec),
+                                                 16, DUAL ? c.to[jj] : c.to[(jj >> 1) & 1],
+                                                 DUAL ? 2 * k0 : jj * c.tstride + 2 * k0, 0, 0);
     }
 }
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+// Fragments of half s (k 32s .. 32s+31) of the block in `buf`.
+template <bool DUAL>
+__device__ __forceinline__ void read_half(const TileCtx& c, const uint4* __restrict__ buf, int s, Frag16& f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4* p = buf + c.rd[2 * s + h];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[8 * h + j] = __builtin_bit_cast(u32x4_t, p[wblk<DUAL>(j)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[8 * h + 4 + i] = __builtin_bit_cast(u32x4_t, p[c.rdt + i * 32 * kChunks]);
+    }
+}
+
+__device__ __forceinline__ void mfma_half(const Frag16& f, f32x16_t (&acc)[4][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f[8 * h + j]),
+                                                                    as_bf16x8(f[8 * h + 4 + i]), acc[j][i], 0, 0, 0);
+}
+
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
-// One stage of the main loop: stage kt lives in `cur`, `nxt` holds stage kt+1
-// and `dma` receives stage kt+3.  LATER = stages issued after kt+1 that may
-// still be in flight (2 in steady state, 1 and 0 at the tail); DMA = whether
-// stage kt+3 exists; NEXT = whether stage kt+1 exists.
-template <bool DUAL, bool ACTIVE, bool DMA, int LATER, bool NEXT>
-__device__ __forceinline__ void stage_step(const TileCtx<DUAL>& c, const uint4* __restrict__ cur,
-                                           const uint4* __restrict__ nxt, uint4* __restrict__ dma,
-                                           int kt, Frags& f0, Frags& f1, f32x16_t (&acc)[4][4]) {
-    if (!ACTIVE) {
-        if (DMA) issue_stage(c, dma, (kt + 3) * kBK);
-        if (NEXT) ring_barrier<LATER * kDmaPerStage>();
-        return;
-    }
-    // First k16 half: its 16 MFMAs carry the reads of the second half's
-    // fragments and the copies of stage kt+3, one between each pair of MFMAs.
-    if (DMA) issue_stage(c, dma, (kt + 3) * kBK);
-    read_frags(c, cur, 1, f1);
-    mfma_range<0, 16>(f0, acc);
+// 32 MFMAs with, after every second one, a fragment read (READ) and a copy (COPY).
+template <bool READ, bool COPY>
+__device__ __forceinline__ void sched_half() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
+        if (READ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (DMA) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+        if (COPY) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // A few MFMAs of the second half stay in the pipe across the barrier.
-    mfma_range<0, 4>(f1, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if (NEXT) {
-        ring_barrier<LATER * kDmaPerStage>();
-        read_frags(c, nxt, 0, f0);
-    }
-    mfma_range<4, 16>(f1, acc);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (NEXT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The K loop over nk stages (nk a multiple of 4, >= 4); stages 0..2 are
-// already being copied into st0..st2.
-template <bool DUAL, bool ACTIVE>
-__device__ __forceinline__ void main_loop(const TileCtx<DUAL>& c, uint4* st0, uint4* st1, uint4* st2,
-                                          uint4* st3, int nk, f32x16_t (&acc)[4][4]) {
-    ring_barrier<2 * kDmaPerStage>();
-    Frags f0, f1;
-    read_frags(c, st0, 0, f0);
-    int kt = 0;
-    for (; kt + 4 < nk; kt += 4) {
-        stage_step<DUAL, ACTIVE, true, 2, true>(c, st0, st1, st3, kt + 0, f0, f1, acc);
-        stage_step<DUAL, ACTIVE, true, 2, true>(c, st1, st2, st0, kt + 1, f0, f1, acc);
-        stage_step<DUAL, ACTIVE, true, 2, true>(c, st2, st3, st1, kt + 2, f0, f1, acc);
-        stage_step<DUAL, ACTIVE, true, 2, true>(c, st3, st0, st2, kt + 3, f0, f1, acc);
+// Block kb (in `cur`) as two 32-k stages.  On entry its first half's fragments
+// are in f0 and, for every wave, the block is complete in `cur`.
+//   first half : read the second half's fragments into f1; MFMAs on f0.
+//   second half: (NEXT) barrier - block kb+1 (copied one block ago) has landed
+//                and every wave has read all of `cur` - then (COPY) copy block
+//                kb+2 into `cur` and read block kb+1's first half into f0 from
+//                `nxt`; MFMAs on f1.
+// The barrier waits for every outstanding copy (vmcnt 0): the only ones are
+// block kb+1's, issued a block earlier.
+template <bool DUAL, bool ACTIVE, bool COPY, bool NEXT>
+__device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__ cur, const uint4* __restrict__ nxt,
+                                           int kb, Frag16& f0, Frag16& f1, f32x16_t (&acc)[4][4]) {
+    if (ACTIVE) {
+        read_half<DUAL>(c, cur, 1, f1);
+        mfma_half(f0, acc);
+        sched_half<true, false>();
     }
-    // last four stages: kt = nk-4 .. nk-1
-    stage_step<DUAL, ACTIVE, true, 2, true>(c, st0, st1, st3, kt + 0, f0, f1, acc);
-    stage_step<DUAL, ACTIVE, false, 1, true>(c, st1, st2, st0, kt + 1, f0, f1, acc);
-    stage_step<DUAL, ACTIVE, false, 0, true>(c, st2, st3, st1, kt + 2, f0, f1, acc);
-    stage_step<DUAL, ACTIVE, false, 0, false>(c, st3, st0, st2, kt + 3, f0, f1, acc);
+    if (NEXT) block_barrier<0>();
+    if (COPY) {
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, cur, (kb + 2) * kBK, j);
+    }
+    if (ACTIVE) {
+        if (NEXT) read_half<DUAL>(c, nxt, 0, f0);
+        mfma_half(f1, acc);
+        sched_half<NEXT, COPY>();
+    }
+}
+
+// The K loop over nb blocks (nb a multiple of 4, >= 4).  Before it: blocks 0
+// and 1 are being copied into b0 and b1.
+template <bool DUAL, bool ACTIVE>
+__device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1, int nb, f32x16_t (&acc)[4][4]) {
+    block_barrier<kCopies>();  // block 0 has landed
+    Frag16 f0, f1;
+    if (ACTIVE) read_half<DUAL>(c, b0, 0, f0);
+    int kb = 0;
+    do {
+        block_step<DUAL, ACTIVE, true, true>(c, b0, b1, kb, f0, f1, acc);
+        block_step<DUAL, ACTIVE, true, true>(c, b1, b0, kb + 1, f0, f1, acc);
+        kb += 2;
+    } while (kb < nb - 2);
+    block_step<DUAL, ACTIVE, false, true>(c, b0, b1, kb, f0, f1, acc);
+    block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, f0, f1, acc);
 }
 
 template <bool DUAL>
@@ -208,82 +217,99 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
-    int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_tt, int n_wt, int GN,
+    int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_tt, int n_wt,
     int ld_out, int n_src, int P, int ksplit, size_t split_stride) {
-    __shared__ uint4 st0[kStageVec];
-    __shared__ uint4 st1[kStageVec];
-    __shared__ uint4 st2[kStageVec];
-    __shared__ uint4 st3[kStageVec];
+    __shared__ uint4 b0[kBufVec];
+    __shared__ uint4 b1[kBufVec];
 
-    // ---- tile of this workgroup
+    // ---- tile of this workgroup.  n_tt * n_wt tiles are launched per K part,
+    // at least as many as the segments hold; the rest exit here.
     const int nblk = gridDim.x;  // a multiple of 8
     const int L_all = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    // K may be cut into `ksplit` parts; part s adds over k in [s*K/ksplit,
-    // (s+1)*K/ksplit) and writes its own output buffer (out + s*split_stride).
     const int split = L_all / (n_tt * n_wt);
-    const int L = L_all - split * (n_tt * n_wt);
+    int L = L_all - split * (n_tt * n_wt);
     if (split >= ksplit) return;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
     out = static_cast<char*>(out) + split * split_stride * (DUAL ? sizeof(bf16_t) : sizeof(float));
-    const int per_group = n_tt * GN;
-    const int grp = L / per_group;
-    const int rem = L - grp * per_group;
-    const int tt = rem / GN;
-    const int wt = grp * GN + (rem - (rem / GN) * GN);
+    // expert e owns tiles [sum of earlier experts' n_tt_e * n_wt, + n_tt_e * n_wt)
+    int e = 0, ntt_e = 0;
+    for (; e < kExperts; ++e) {
+        ntt_e = (offsets[e + 1] - offsets[e]) / kTT;  // segments are padded to kTT rows
+        if (L < ntt_e * n_wt) break;
+        L -= ntt_e * n_wt;
+    }
+    if (e == kExperts) return;
+    // groups of gn weight tiles x the expert's ntt_e token tiles, token-major
+    const int gn = max(1, min(n_wt, kXcdTiles / ntt_e));
+    const int g = L / (gn * ntt_e);
+    const int rem = L - g * gn * ntt_e;
+    const int gw = min(gn, n_wt - g * gn);  // the last group may be narrower
+    const int ttl = rem / gw;
+    const int wt = g * gn + (rem - ttl * gw);
 
-    const int p0 = tt * kTT;
-    if (p0 >= offsets[kExperts]) return;
-    const int e = expert_of_row(offsets, p0);
+    const int p0 = offsets[e] + ttl * kTT;
     const int row_end = min(offsets[e + 1], P);
     const int valid = min(min(kTT, offsets[e] + counts[e] - p0), row_end - p0);
     if (valid <= 0) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_w = wave & 1;
     const int wave_t = wave >> 1;
+    const int fr = lane & 31;  // fragment row / token column of this lane
+    const int fk = lane >> 5;  // k-group of this lane within a k16 half
 
-    // ---- copy assignment: wave w copies weight rows and token rows
-    // [w*64, w*64+64) in 4 blocks of 16 rows; lane l of a block writes LDS row
-    // (block row + l/4), physical chunk l%4, so it reads logical chunk
-    // (l%4) ^ g(row).
-    TileCtx<DUAL> c;
+    TileCtx c;
     {
-        const int first_src = DUAL ? row_src[p0] : 0;
+        // Copies: wave w fills LDS rows w*64 .. +64 of the weight half and of
+        // the token half as 8 groups of 8 rows; lane l of group j writes row
+        // w*64 + 8j + l/8, physical chunk l%8, so it reads logical chunk
+        // (l%8) ^ g(row).  g() of that row depends on l and on j's bit 1 only.
+        const int rl = lane >> 3;
+        const int ch0 = (lane & 7) ^ swz(rl);
+        const int ch1 = (lane & 7) ^ swz(16 + rl);
+        // Gate/up: LDS weight rows 0-127 (waves 0, 1) are w1 rows, 128-255
+        // (waves 2, 3) the same rows of w3.
+        const bf16_t* wm = (DUAL && wave >= 2) ? wb : wa;
+        const int wrow = DUAL ? wt * (kTW / 2) + (wave & 1) * 64 : wt * kTW + wave * 64;
+        c.wres = make_rsrc(wm + (static_cast<size_t>(e) * Nw + wrow) * Kdim + kbase);
+        c.wo[0] = (static_cast<uint32_t>(rl) * Kdim + 8u * ch0) * 2u;
+        c.wo[1] = (static_cast<uint32_t>(rl) * Kdim + 8u * ch1) * 2u;
+        c.wstride = 8 * Kdim * 2;
+        if (DUAL) {
+            // gathered rows of x; padding rows copy the tile's first row
+            c.tres = make_rsrc(act + kbase);
+            const int first_src = row_src[p0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wave * 64 + j * 16 + (lane >> 2);
-            const int chunk = (lane & 3) ^ swz(r);
-            if (DUAL) {
-                const int f0 = wt * (kTW / 2);
-                const bf16_t* base = (r < kTW / 2) ? wa : wb;
-                c.gw[j] = base + (static_cast<size_t>(e) * Nw + f0 + (r & (kTW / 2 - 1))) * Kdim + kbase + 8 * chunk;
+            for (int j = 0; j < 8; ++j) {
+                const int r = wave * 64 + 8 * j + rl;
                 int src = (r < valid) ? row_src[p0 + r] : first_src;
                 if (src < 0 || src >= n_src) src = first_src;
                 if (src < 0 || src >= n_src) src = 0;
-                c.gt[j] = act + static_cast<size_t>(src >> 1) * ld_act + kbase + 8 * chunk;
-            } else {
-                c.gw[j] = wa + (static_cast<size_t>(e) * Nw + wt * kTW + r) * Kdim + kbase + 8 * chunk;
-                const int pr = (r < valid) ? p0 + r : p0;
-                c.gt[j] = act + static_cast<size_t>(pr) * ld_act + kbase + 8 * chunk;
+                c.to[j] = static_cast<uint32_t>(
+                    (static_cast<size_t>(src >> 1) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
             }
-        }
-        c.dma_w = (wave * 64) * kChunks;
-        c.dma_t = (kTW + wave * 64) * kChunks;
-        const int fr = lane & 31;
-        const int fk = lane >> 5;
-        c.rd[0] = fr * kChunks + ((0 + fk) ^ swz(fr));
-        c.rd[1] = fr * kChunks + ((2 + fk) ^ swz(fr));
+            c.tstride = 0;
+        } else {
+            // the tile's 256 rows of h, padding rows included (all inside the
+            // expert's padded segment, hence inside h)
+            c.tres = make_rsrc(act + static_cast<size_t>(p0 + wave * 64) * ld_act + kbase);
+            c.to[0] = (static_cast<uint32_t>(rl) * ld_act + 8u * ch0) * 2u;
+            c.to[1] = (static_cast<uint32_t>(rl) * ld_act + 8u * ch1) * 2u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rowb = DUAL ? ((j < 2 ? 0 : kTW / 2) + wave_w * 64 + (j & 1) * 32) : (wave_w * 128 + j * 32);
-            c.wblk[j] = rowb * kChunks;
+            for (int j = 2; j < 8; ++j) c.to[j] = 0;
+            c.tstride = 8 * ld_act * 2;
         }
-        c.tblk0 = (kTW + wave_t * 128) * kChunks;
+        c.dma = wave * 64 * kChunks;
+        // Fragment reads: blocks start at multiples of 32 rows, so g() of a
+        // block row is g(fr).  Logical chunk of half s, k16 half h: 4s + 2h + fk.
+        const int row0 = wave_w * (DUAL ? 64 : 128) + fr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c.rd[q] = row0 * kChunks + ((2 * q + fk) ^ swz(fr));
+        c.rdt = (kTW + wave_t * 128 - wave_w * (DUAL ? 64 : 128)) * kChunks;
     }
-    const bool active = __builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0;
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -293,25 +319,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
 
-    const int nk = kpart / kBK;  // a multiple of 4
-    issue_stage(c, st0, 0);
-    issue_stage(c, st1, kBK);
-    issue_stage(c, st2, 2 * kBK);
-    if (active)
-        main_loop<DUAL, true>(c, st0, st1, st2, st3, nk, acc);
+    const int nb = kpart / kBK;  // a multiple of 4, >= 4 (K parts are multiples of 256)
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, b0, 0, j);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
+    // A wave whose 128 token rows are all padding skips its reads and MFMAs.
+    if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0)
+        main_loop<DUAL, true>(c, b0, b1, nb, acc);
     else
-        main_loop<DUAL, false>(c, st0, st1, st2, st3, nk, acc);
+        main_loop<DUAL, false>(c, b0, b1, nb, acc);
 
     // ---- epilogue.  32x32 C layout: lane l holds token column l%32 and weight
     // rows 8*(q/4) + 4*(l/32) + q%4 of each block, q = 0..15.
-    const int fr = lane & 31;
-    const int fk = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wave_t * 128 + i * 32 + fr;  // token row within the tile
-        const int p = p0 + r;
+        const int rt = wave_t * 128 + i * 32 + fr;  // token row within the tile
+        const int p = p0 + rt;
         if (p >= row_end) continue;
-        const bool real = r < valid;
+        const bool real = rt < valid;
         if (DUAL) {
             bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
             const int fb = wt * (kTW / 2) + wave_w * 64;
@@ -345,13 +371,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-int group_size(int n_wt) {
-    for (int g = 8; g > 1; g >>= 1)
-        if (n_wt % g == 0) return g;
-    return 1;
-}
-
 }  // namespace
+
+bool tiled_fits(const Shape& s) {
+    return static_cast<unsigned long long>(s.T) * s.d * 2 + 2ull * s.d < (1ull << 32);
+}
 
 int tiled_down_ksplit(const Shape& s) {
     // Cut the down projection's K in two when its tiles would not fill four
@@ -365,21 +389,21 @@ int tiled_down_ksplit(const Shape& s) {
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
                         void* out, hipStream_t st, int ksplit) {
+    if (!tiled_fits(s)) return hipErrorInvalidValue;
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = gate_up ? s.F / (kTW / 2) : s.d / kTW;
-    const int GN = group_size(n_wt);
     const int G = (n_tt * n_wt * ksplit + 7) / 8 * 8;
     const size_t split_stride = static_cast<size_t>(P) * (gate_up ? s.F : s.d);
     if (gate_up)
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
                                               static_cast<const bf16_t*>(wa), static_cast<const bf16_t*>(wb),
-                                              out, s.d, s.F, s.d, n_tt, n_wt, GN, s.F, s.T * s.K, P,
+                                              out, s.d, s.F, s.d, n_tt, n_wt, s.F, s.T * s.K, P,
                                               ksplit, split_stride);
     else
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
-                                               n_tt, n_wt, GN, s.d, s.T * s.K, P, ksplit, split_stride);
+                                               n_tt, n_wt, s.d, s.T * s.K, P, ksplit, split_stride);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def test_header_and_library_agree():
         assert hasattr(lib, name), name
 
 
-def test_north_star_entry_points_present():
+def test_layer_entry_points_present():
     for name in ("moe_router_topk", "moe_permute", "moe_grouped_swiglu", "moe_combine",
                  "moe_layer_forward"):
         assert name in header_functions()
@@ -57,6 +57,13 @@ def test_sizes():
     assert moe.moe_max_permuted_rows(d, 4096, 256) == 8192 + 8 * 255
     assert moe.moe_max_permuted_rows(d, 32, 0) == 64 + 8 * 15
     assert moe.moe_max_permuted_rows(d, 32, 100) == -1
+    # tile 256 reaches x rows through 32-bit byte offsets: T * d * 2 (plus
+    # one row of k offsets) must stay below 4 GiB
+    T_big = (1 << 32) // (4096 * 2) - 1
+    assert moe.moe_default_tile_m(d, T_big - 1) == 256
+    assert moe.moe_default_tile_m(d, T_big) == 16
+    assert moe.moe_max_permuted_rows(d, T_big, 256) == -1
+    assert moe.moe_max_permuted_rows(d, T_big, 16) == 2 * T_big + 8 * 15
     ws = moe.moe_workspace_size(d, 4096, 0)
     P = 8192 + 8 * 255
     assert ws >= P * 14336 * 2 + P * 4096 * 4
