@@ -36,9 +36,10 @@
 //     0-7 with 16-23, 8-15 with 24-31, measured with SQ_LDS_BANK_CONFLICT);
 //     in each phase the 8 even rows and the 8 odd rows get 8 distinct chunks,
 //     so the phase covers all 64 banks.  The copies write whole 1 KB runs.
-//   * Tile order: workgroup b runs on XCD b % 8, and each XCD gets a contiguous
-//     run of an expert-major enumeration (computed on the device from the
-//     segment offsets): expert by expert, groups of G weight tiles x all of the
+//   * Tile order: workgroup b runs on XCD b % 8, and each XCD gets an equal
+//     contiguous run of an expert-major enumeration of the tiles the segments
+//     actually hold (computed on the device from the segment offsets; the grid
+//     is sized for the worst case and the spare workgroups exit): expert by expert, groups of G weight tiles x all of the
 //     expert's token tiles, G ~ 32 / (the expert's token tiles).  The ~32 tiles
 //     an XCD runs at once (32 CUs) then read the same few weight and token
 //     tiles, so each k-slice comes from HBM once and from its L2 after that.
@@ -217,18 +218,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
-    int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_tt, int n_wt,
+    int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_wt,
     int ld_out, int n_src, int P, int ksplit, size_t split_stride) {
     __shared__ uint4 b0[kBufVec];
     __shared__ uint4 b1[kBufVec];
 
-    // ---- tile of this workgroup.  n_tt * n_wt tiles are launched per K part,
-    // at least as many as the segments hold; the rest exit here.
-    const int nblk = gridDim.x;  // a multiple of 8
-    const int L_all = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int split = L_all / (n_tt * n_wt);
-    int L = L_all - split * (n_tt * n_wt);
-    if (split >= ksplit) return;
+    // ---- tile of this workgroup.  The grid covers the worst case (P_max / 256
+    // token tiles x n_wt per K part); the segments hold fewer.  Those tiles are dealt out
+    // evenly: XCD x (workgroups b with b % 8 == x) takes a contiguous run of
+    // ceil(total / 8) of them, and the remaining workgroups exit here.
+    int per_split = 0;
+#pragma unroll
+    for (int j = 0; j < kExperts; ++j) per_split += (offsets[j + 1] - offsets[j]) / kTT * n_wt;
+    const int total = per_split * ksplit;
+    const int run = (total + 7) >> 3;
+    if (static_cast<int>(blockIdx.x >> 3) >= run) return;
+    const int L_all = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
+    if (L_all >= total) return;
+    const int split = L_all / per_split;
+    int L = L_all - split * per_split;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
     out = static_cast<char*>(out) + split * split_stride * (DUAL ? sizeof(bf16_t) : sizeof(float));
@@ -398,12 +406,12 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
     if (gate_up)
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
                                               static_cast<const bf16_t*>(wa), static_cast<const bf16_t*>(wb),
-                                              out, s.d, s.F, s.d, n_tt, n_wt, s.F, s.T * s.K, P,
+                                              out, s.d, s.F, s.d, n_wt, s.F, s.T * s.K, P,
                                               ksplit, split_stride);
     else
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
-                                               n_tt, n_wt, s.d, s.T * s.K, P, ksplit, split_stride);
+                                               n_wt, s.d, s.T * s.K, P, ksplit, split_stride);
     return hipGetLastError();
 }
 
