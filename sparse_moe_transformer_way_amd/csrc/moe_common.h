@@ -46,8 +46,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// SiLU(z) = z * sigmoid(z) in fp32 with the accurate exp.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) in fp32 from the hardware base-2 exponential
+// (v_exp_f32) and reciprocal (v_rcp_f32), each within about one ulp, instead
+// of the library expf and a true division: four VALU operations instead of
+// about twenty, which matters in the gate/up epilogue (128 SiLUs per lane).
+// e^-z overflowing to +inf gives z * 0 = -0, the limit for z -> -inf.
+__device__ __forceinline__ float silu_f32(float z) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
+}
 
 // ---------------------------------------------------------------------------
 // Internal launchers (host side).  Each enqueues on `stream` and returns the
