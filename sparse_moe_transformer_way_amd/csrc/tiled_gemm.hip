@@ -349,14 +349,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (DUAL) {
             bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
             const int fb = wt * (kTW / 2) + wave_w * 64;
+            // padding rows are written as zeros; a bit mask (not a branch or
+            // a multiply) clears them, whatever their accumulators hold
+            const uint32_t keep = real ? 0xffffffffu : 0u;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     float v[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        v[u] = real ? silu_f32(acc[jj][i][4 * q4 + u]) * acc[jj + 2][i][4 * q4 + u] : 0.0f;
+                    for (int u = 0; u < 4; ++u) {
+                        const float hv = silu_f32(acc[jj][i][4 * q4 + u]) * acc[jj + 2][i][4 * q4 + u];
+                        v[u] = __uint_as_float(__float_as_uint(hv) & keep);
+                    }
                     uint2 o;
                     o.x = pack_bf16x2(v[0], v[1]);
                     o.y = pack_bf16x2(v[2], v[3]);
