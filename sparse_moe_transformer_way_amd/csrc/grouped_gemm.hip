@@ -42,28 +42,120 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
     return e;
 }
 
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
 // ===========================================================================
 // Weight-streaming kernel (bf16, tile_m = 16)
 // ===========================================================================
 //
-// Block = 4 waves, one expert (blockIdx.y), one slab of kRB*16 weight rows
-// (blockIdx.x).  Wave w covers K range [w*K/4, (w+1)*K/4) in super-steps of 128.
-// Load j (0..3) of a super-step gives lane (r = l%16, g = l/16) the 8 elements
-// k = base + 32j + 8g .. +8 of weight row r of a 16-row block, so one load
-// instruction reads 64 contiguous bytes of each of 16 rows (this streams at
-// ~5.9 TB/s on MI355X, against ~3.6 TB/s when each lane instead reads 64
-// contiguous bytes by itself).  The activation rows are loaded the same way and
-// MFMA j pairs load j of both operands: the contraction pairs equal k on both
-// sides, so this permutation of k is exact.
+// Block = 4 waves, one expert (blockIdx.y), one slab of 64 weight rows
+// (blockIdx.x).  Wave w covers the K range [w*K/4, (w+1)*K/4) in stages of 64.
+// A stage of the wave's 64 rows (8 KB) is copied into the wave's own slice of
+// LDS by buffer loads with the LDS destination bit, 8 rows x 128 bytes per
+// instruction, so each request is a whole 128-byte line (streams at ~6.8 TB/s
+// on MI355X, against ~5.9 TB/s for the 16 rows x 64 bytes that loading
+// straight into MFMA operand registers allows).  Two stage buffers per wave:
+// stage s+1 is copied while stage s is read and multiplied.  No wave reads
+// another wave's slice, so there are no barriers in the K loop: the
+// compiler's wait for the copy into the buffer a read names is the only
+// synchronisation, and each stage's copy is issued after that stage's reads
+// so the wait never covers the next copy.
 //
-// DUAL (gate/up): row blocks 0,1 are w1 rows f0..f0+31, blocks 2,3 are w3 rows
-// f0..f0+31; the epilogue forms SiLU(a1) * a3.  Otherwise (down): 4 blocks of
-// w2 rows j0..j0+63, fp32 output.
+// Fragments: MFMA 16x16x32, weights as the A operand.  In 32-k step t of a
+// stage, lane (r = l%16, g = l/16) takes row r of a 16-row block at logical
+// chunk 4t + g (k = 32t + 8g .. +8); the activation rows are read straight
+// from global memory (they are few and L2-resident) at the same k.  Chunk c
+// of LDS row r sits at c ^ f(r), f(r) = 2 * ((r >> 1) & 3): in each 16-lane
+// phase of a fragment read (lanes 0-7 with 16-23) the even rows and the odd
+// rows each get 8 distinct chunks, so the phase covers all 64 banks.
+//
+// DUAL (gate/up): rows 0-31 of the slab are w1 rows f0..f0+31, rows 32-63 the
+// same rows of w3; the epilogue forms SiLU(a1) * a3.  Otherwise (down): w2 rows
+// j0..j0+63, fp32 output.
 
-constexpr int kStreamRB = 4;     // 16-row weight blocks per wave
-constexpr int kStreamMaxTB = 4;  // 16-row token blocks per pass
+constexpr int kStreamRB = 4;       // 16-row weight blocks per wave
+constexpr int kStreamMaxTB = 4;    // 16-row token blocks per pass
+constexpr int kStreamWaveVec = 512;  // uint4 of one wave's stage slice (64 rows x 128 B)
+
+typedef void __attribute__((address_space(3)))* lds_ptr_t;
+
+__device__ __forceinline__ int stream_swz(int row) { return ((row >> 1) & 3) << 1; }
+
+// Buffer resource over [base, base + 4 GiB) for a wave-uniform base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base) {
+    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting of gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+
+struct StreamCtx {
+    __amdgpu_buffer_rsrc_t wres[2];  // weight rows 0-31 and 32-63 of the slab (k origin: the wave's range)
+    uint32_t wo;                     // lane byte offset of its copy source within an 8-row group
+    int wgrp;                        // bytes between 8-row groups
+    int slice;                       // uint4 offset of this wave's stage slice
+    int rd[2];                       // per 32-k step: uint4 index of this lane's fragment in block 0
+};
+
+// Copy stage s (k = 64s .. 64s+63 of the wave's range) into `buf`.
+__device__ __forceinline__ void stream_copy(const StreamCtx& c, uint4* __restrict__ buf, int s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        // address-space conversion needs a C-style cast
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.wres[j >> 2], (lds_ptr_t)(buf + c.slice + j * 64), 16, c.wo,
+                                                 (j & 3) * c.wgrp + 128 * s, 0, 0);
+}
+
+typedef const __attribute__((address_space(1))) u32x4_t* gvec_t;
+
+// One stage: token fragments from global memory, weight fragments from `cur`,
+// then (COPY) the next stage's copy into `nxt`, then the MFMAs.  Every lane
+// loads a real row (arow) and masks it (amask: all ones, or zero for a row
+// past the segment), so the loads stay plain global loads without branches.
+template <int NTP, bool COPY>
+__device__ __forceinline__ void stream_stage(const StreamCtx& c, const uint4* __restrict__ cur,
+                                             uint4* __restrict__ nxt, int s,
+                                             const bf16_t* const (&arow)[kStreamMaxTB],
+                                             const uint32_t (&amask)[kStreamMaxTB],
+                                             f32x4_t (&acc)[kStreamMaxTB][kStreamRB]) {
+    u32x4_t tv[NTP][2];
+#pragma unroll
+    for (int tb = 0; tb < NTP; ++tb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) tv[tb][t] = *(gvec_t)(arow[tb] + 64 * s + 32 * t);
+#pragma unroll
+    for (int tb = 0; tb < NTP; ++tb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) tv[tb][t] &= amask[tb];
+    u32x4_t wv[2][kStreamRB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < kStreamRB; ++b) wv[t][b] = __builtin_bit_cast(u32x4_t, cur[c.rd[t] + b * 128]);
+    if (COPY) stream_copy(c, nxt, s + 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int tb = 0; tb < NTP; ++tb)
+#pragma unroll
+                for (int b = 0; b < kStreamRB; ++b)
+                    acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[t][b]), as_bf16x8(tv[tb][t]),
+                                                                         acc[tb][b], 0, 0, 0);
+    // keep the next stage's reads (which wait for its copy) after these MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop of one pass over NTP token blocks: ns stages (ns even, >= 2).
+template <int NTP>
+__device__ __forceinline__ void stream_k_loop(const StreamCtx& c, uint4* sb0, uint4* sb1, int ns,
+                                              const bf16_t* const (&arow)[kStreamMaxTB],
+                                              const uint32_t (&amask)[kStreamMaxTB],
+                                              f32x4_t (&acc)[kStreamMaxTB][kStreamRB]) {
+    stream_copy(c, sb0, 0);
+    int s = 0;
+    for (; s + 2 < ns; s += 2) {
+        stream_stage<NTP, true>(c, sb0, sb1, s, arow, amask, acc);
+        stream_stage<NTP, true>(c, sb1, sb0, s + 1, arow, amask, acc);
+    }
+    stream_stage<NTP, true>(c, sb0, sb1, s, arow, amask, acc);
+    stream_stage<NTP, false>(c, sb1, sb0, s + 1, arow, amask, acc);
+}
 
 template <bool DUAL>
 __global__ __launch_bounds__(256) void stream_kernel(
@@ -71,7 +163,10 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P) {
-    __shared__ f32x4_t red[4][kStreamMaxTB][kStreamRB][64];  // 64 KB
+    // Two stage buffers (each 4 wave slices of 8 KB); after the K loop they
+    // hold the cross-wave reduction [wave][token block][weight block][lane].
+    __shared__ uint4 sb0[4 * kStreamWaveVec];
+    __shared__ uint4 sb1[4 * kStreamWaveVec];
 
     const int e = blockIdx.y;
     const int seg = offsets[e];
@@ -82,44 +177,61 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int ntb = (cnt + 15) >> 4;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int r = lane & 15;
     const int g = lane >> 4;
     const int kq = Kdim >> 2;
     const int kbeg = wave * kq;
+    const int ns = kq / 64;  // even (K is a multiple of 512)
 
-    // Weight row pointers of this lane's 4 row blocks.
-    const bf16_t* wrow[kStreamRB];
-    if (DUAL) {
-        const int f0 = blockIdx.x * 32;
-#pragma unroll
-        for (int b = 0; b < kStreamRB; ++b) {
-            const bf16_t* base = (b < 2) ? wa : wb;
-            wrow[b] = base + (static_cast<size_t>(e) * Nw + f0 + (b & 1) * 16 + r) * Kdim + 8 * g;
+    StreamCtx c;
+    {
+        // copy lane l: row l/8 of an 8-row group, physical chunk l%8, so it
+        // reads logical chunk (l%8) ^ f(row) (f depends on the row's low bits only)
+        const int rl = lane >> 3;
+        const int lch = (lane & 7) ^ stream_swz(rl);
+        c.wo = (static_cast<uint32_t>(rl) * Kdim + 8u * lch) * 2u;
+        c.wgrp = 8 * Kdim * 2;
+        if (DUAL) {
+            const size_t f0 = static_cast<size_t>(e) * Nw + blockIdx.x * 32;
+            c.wres[0] = stream_rsrc(wa + f0 * Kdim + kbeg);
+            c.wres[1] = stream_rsrc(wb + f0 * Kdim + kbeg);
+        } else {
+            const size_t j0 = static_cast<size_t>(e) * Nw + blockIdx.x * 64;
+            c.wres[0] = stream_rsrc(wa + j0 * Kdim + kbeg);
+            c.wres[1] = stream_rsrc(wa + (j0 + 32) * Kdim + kbeg);
         }
-    } else {
-        const int j0 = blockIdx.x * 64;
+        c.slice = wave * kStreamWaveVec;
 #pragma unroll
-        for (int b = 0; b < kStreamRB; ++b)
-            wrow[b] = wa + (static_cast<size_t>(e) * Nw + j0 + b * 16 + r) * Kdim + 8 * g;
+        for (int t = 0; t < 2; ++t) c.rd[t] = c.slice + r * 8 + ((4 * t + g) ^ stream_swz(r));
     }
 
     for (int tb0 = 0; tb0 < ntb; tb0 += kStreamMaxTB) {
         const int ntp = min(kStreamMaxTB, ntb - tb0);
-        // Activation row of this lane in each token block (nullptr = zero row).
+        // Activation row of this lane in each token block, at the wave's k
+        // origin and this lane's k-group; rows past the segment read the
+        // segment's first row and are masked to zero.
         const bf16_t* arow[kStreamMaxTB];
+        uint32_t amask[kStreamMaxTB];
+        const int src0 = DUAL ? row_src[seg] : 0;
+        const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? (src0 >> 1) : 0) : seg;
 #pragma unroll
         for (int tb = 0; tb < kStreamMaxTB; ++tb) {
-            arow[tb] = nullptr;
             const int p = seg + (tb0 + tb) * 16 + r;
-            if (tb < ntp) {
+            int row = row0;
+            bool real = false;
+            if (tb < ntp && p < seg + cnt) {
                 if (DUAL) {
-                    const int src = (p < seg + cnt) ? row_src[p] : -1;
-                    if (src >= 0 && src < n_src) arow[tb] = act + static_cast<size_t>(src >> 1) * ld_act + 8 * g;
-                } else if (p < seg + cnt) {
-                    arow[tb] = act + static_cast<size_t>(p) * ld_act + 8 * g;
+                    const int src = row_src[p];
+                    real = src >= 0 && src < n_src;
+                    if (real) row = src >> 1;
+                } else {
+                    real = true;
+                    row = p;
                 }
             }
+            arow[tb] = act + static_cast<size_t>(row) * ld_act + kbeg + 8 * g;
+            amask[tb] = real ? 0xffffffffu : 0u;
         }
 
         f32x4_t acc[kStreamMaxTB][kStreamRB];
@@ -128,50 +240,36 @@ __global__ __launch_bounds__(256) void stream_kernel(
 #pragma unroll
             for (int b = 0; b < kStreamRB; ++b) acc[tb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int k = kbeg; k < kbeg + kq; k += 128) {
-            u32x4_t wv[kStreamRB][4];
-#pragma unroll
-            for (int b = 0; b < kStreamRB; ++b) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    wv[b][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wrow[b] + k + 32 * j));
-            }
-#pragma unroll
-            for (int tb = 0; tb < kStreamMaxTB; ++tb) {
-                if (tb < ntp) {
-                    uint4 av[4];
-                    if (arow[tb] != nullptr) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const uint4*>(arow[tb] + k + 32 * j);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) av[j] = zero4();
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int b = 0; b < kStreamRB; ++b)
-                            acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(wv[b][j]), as_bf16x8(av[j]), acc[tb][b], 0, 0, 0);
-                }
-            }
+        switch (ntp) {
+            case 1: stream_k_loop<1>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 2: stream_k_loop<2>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 3: stream_k_loop<3>(c, sb0, sb1, ns, arow, amask, acc); break;
+            default: stream_k_loop<4>(c, sb0, sb1, ns, arow, amask, acc); break;
         }
 
-        // Cross-wave K reduction in a fixed order, then wave w finishes token block w.
+        // Cross-wave K reduction in a fixed order through the stage buffers,
+        // then wave w finishes token block w.
+        __syncthreads();
+        f32x4_t* red0 = reinterpret_cast<f32x4_t*>(sb0);  // waves 0, 1
+        f32x4_t* red1 = reinterpret_cast<f32x4_t*>(sb1);  // waves 2, 3
+        auto red = [&](int w, int tb, int b) -> f32x4_t& {
+            const int i = (((w & 1) * kStreamMaxTB + tb) * kStreamRB + b) * 64 + lane;
+            return (w < 2 ? red0 : red1)[i];
+        };
 #pragma unroll
         for (int tb = 0; tb < kStreamMaxTB; ++tb)
             if (tb < ntp)
 #pragma unroll
-                for (int b = 0; b < kStreamRB; ++b) red[wave][tb][b][lane] = acc[tb][b];
+                for (int b = 0; b < kStreamRB; ++b) red(wave, tb, b) = acc[tb][b];
         __syncthreads();
         if (wave < ntp && seg + (tb0 + wave) * 16 + r < seg_end) {
             const int tb = wave;
-            f32x4_t s[kStreamRB];
+            f32x4_t sum[kStreamRB];
 #pragma unroll
             for (int b = 0; b < kStreamRB; ++b) {
-                s[b] = red[0][tb][b][lane];
+                sum[b] = red(0, tb, b);
 #pragma unroll
-                for (int w = 1; w < 4; ++w) s[b] += red[w][tb][b][lane];
+                for (int w = 1; w < 4; ++w) sum[b] += red(w, tb, b);
             }
             // C layout of 16x16 MFMA: lane l holds column (token) l%16 and rows
             // (weight rows) 4*(l/16) + i, i = 0..3.
@@ -181,7 +279,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * Nw;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const f32x4_t a1 = s[half], a3 = s[half + 2];
+                    const f32x4_t a1 = sum[half], a3 = sum[half + 2];
                     uint2 o;
                     o.x = pack_bf16x2(silu_f32(a1[0]) * a3[0], silu_f32(a1[1]) * a3[1]);
                     o.y = pack_bf16x2(silu_f32(a1[2]) * a3[2], silu_f32(a1[3]) * a3[3]);
@@ -192,7 +290,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 float* yrow = static_cast<float*>(out) + static_cast<size_t>(p) * Nw;
 #pragma unroll
                 for (int b = 0; b < kStreamRB; ++b)
-                    *reinterpret_cast<f32x4_t*>(yrow + j0 + b * 16 + 4 * g) = s[b];
+                    *reinterpret_cast<f32x4_t*>(yrow + j0 + b * 16 + 4 * g) = sum[b];
             }
         }
         __syncthreads();
