@@ -7,7 +7,8 @@
 // softmax).  Softmax of a vector whose other entries are -inf reduces to the
 // two-term form g0 = 1/(1+e), g1 = e/(1+e), e = exp(l_second - l_first).
 //
-// Layout: a block of 4 waves handles 8 tokens; the d channels are cut into
+// Layout: a block of 4 waves handles TOK tokens (8, or 1 for small batches so
+// that a decode step still spreads over T blocks); the d channels are cut into
 // 8-channel chunks and wave w takes the w-th quarter of the chunks, so a token's
 // dot products are spread over 256 lanes (few sequential steps even at decode
 // batch sizes).  Lane j of a wave covers chunks j, j+64, ... of its quarter:
@@ -23,10 +24,10 @@ namespace moe {
 namespace {
 
 constexpr int kExperts = 8;
-constexpr int kTok = 8;           // tokens per block
 constexpr int kWaves = 4;         // waves per block, splitting d
+constexpr int kSmallT = 256;      // up to this many tokens: one token per block
 
-template <bool BF16>
+template <bool BF16, int kTok>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ xv,
                                                           const float* __restrict__ wg, int T,
                                                           int d, int32_t* __restrict__ idx,
@@ -132,11 +133,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
 
 hipError_t launch_router_topk(const Shape& s, const void* x, const float* wg, int32_t* idx,
                               float* gate, float* logits, hipStream_t st) {
-    const int blocks = (s.T + kTok - 1) / kTok;
-    if (s.bf16)
-        router_topk_kernel<true><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
-    else
-        router_topk_kernel<false><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+    // Each block reads all of W_g (d x 8 fp32, from L2): one token per block
+    // for small batches, eight when W_g reuse matters more than parallelism.
+    if (s.T <= kSmallT) {
+        if (s.bf16)
+            router_topk_kernel<true, 1><<<s.T, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+        else
+            router_topk_kernel<false, 1><<<s.T, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+    } else {
+        const int blocks = (s.T + 7) / 8;
+        if (s.bf16)
+            router_topk_kernel<true, 8><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+        else
+            router_topk_kernel<false, 8><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+    }
     return hipGetLastError();
 }
 
