@@ -31,7 +31,9 @@ def layer(T, d, F, dtype, seed=0, workload=200):
 # Router
 # ---------------------------------------------------------------------------
 
+# T <= 256 runs one token per block, larger T eight: 256 and 257 straddle the switch
 @pytest.mark.parametrize("dtype,T,d", [("f32", 64, 128), ("bf16", 37, 512), ("bf16", 1, 4096),
+                                       ("bf16", 256, 512), ("bf16", 257, 512),
                                        ("bf16", 1000, 512), ("f32", 17, 8)])
 def test_router(dtype, T, d):
     inp = layer(T, d, 512, dtype, seed=T)
