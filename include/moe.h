@@ -29,7 +29,8 @@
  *   - Tensor shapes: x [T, d]; W_g [d, n] fp32; w1, w3 [n, F, d]; w2 [n, d, F];
  *     y [T, d].  Activations and expert weights share one dtype (fp32 or bf16);
  *     W_g is always fp32.  Accumulation is fp32 throughout.
- *   - Supported in this version: n_experts == 8, top_k == 2.
+ *   - Supported: 1 <= top_k <= n_experts, n_experts <= 16, top_k <= 4 (Mixtral
+ *     itself is n_experts = 8, top_k = 2; larger values return MOE_ERR_UNSUPPORTED).
  *       fp32: d % 8 == 0, F % 8 == 0.
  *       bf16: d % 512 == 0, F % 512 == 0 (the Mixtral shape d=4096, F=14336 qualifies).
  *     Other shapes return MOE_ERR_UNSUPPORTED.
@@ -49,7 +50,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARGUMENT = 1,   /* null required pointer, negative size, bad tile_m ... */
-    MOE_ERR_UNSUPPORTED = 2,        /* valid but not implemented (n != 8, K != 2, shape) */
+    MOE_ERR_UNSUPPORTED = 2,        /* valid but not implemented (n > 16, K > 4, shape) */
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,
     MOE_ERR_HIP = 4                 /* the HIP runtime reported an error at launch */
 } moe_status_t;

@@ -6,5 +6,5 @@ by the bench's CPU-baseline leg, never by the library.  See moe_oracle.py.
 from .moe_oracle import (  # noqa: F401
     router_logits, topk_indices, topk_mask, softmax, gating, silu, swiglu_expert,
     moe_layer, rmsnorm, round_bf16, moe_block, max_permuted_rows, group_by_expert,
-    expert_rows, combine, routing_margin, top_gap,
+    expert_rows, combine, routing_margin, top_gap, slot_order_gap,
 )

@@ -245,9 +245,12 @@ def combine(y_perm, row_of, gates, residual=None):
 
 def routing_margin(x, wg, K: int = 2) -> np.ndarray:
     """Per token, l_(K) - l_(K+1): the gap between the K-th and (K+1)-th largest
-    logit, computed in float64 from the exact input values."""
+    logit, computed in float64 from the exact input values; +inf when K = n
+    (every expert is selected, so there is no decision to separate)."""
     l = np.asarray(x, np.float64) @ np.asarray(wg, np.float64)
     s = -np.sort(-l, axis=1)
+    if K >= l.shape[1]:
+        return np.full(l.shape[0], np.inf)
     return s[:, K - 1] - s[:, K]
 
 
@@ -256,3 +259,14 @@ def top_gap(x, wg) -> np.ndarray:
     l = np.asarray(x, np.float64) @ np.asarray(wg, np.float64)
     s = -np.sort(-l, axis=1)
     return s[:, 0] - s[:, 1]
+
+
+def slot_order_gap(x, wg, K: int = 2) -> np.ndarray:
+    """Per token, the smallest gap l_(s) - l_(s+1), s = 1..K-1, between
+    neighbouring selected logits in float64: where it is large enough the slot
+    order of the K selected experts is fixed.  +inf for K = 1."""
+    l = np.asarray(x, np.float64) @ np.asarray(wg, np.float64)
+    s = -np.sort(-l, axis=1)
+    if K < 2:
+        return np.full(l.shape[0], np.inf)
+    return (s[:, :K - 1] - s[:, 1:K]).min(axis=1)

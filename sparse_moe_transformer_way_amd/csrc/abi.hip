@@ -25,7 +25,7 @@ moe_status_t check_desc(const moe_layer_desc_t* d) {
     if (d->weight_dtype != MOE_F32 && d->weight_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (d->d_model % 8 != 0 || d->d_ffn % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
     if (d->act_dtype != d->weight_dtype) return MOE_ERR_UNSUPPORTED;
-    if (d->n_experts != 8 || d->top_k != 2) return MOE_ERR_UNSUPPORTED;
+    if (d->n_experts > moe::kMaxExperts || d->top_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
     if (d->act_dtype == MOE_BF16 && (d->d_model % 512 != 0 || d->d_ffn % 512 != 0))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;

@@ -1,8 +1,8 @@
-// Gate-weighted combine of the two expert outputs (+ optional residual) and the
-// unit-gain RMSNorm of the decoder block.
+// Gate-weighted combine of the K selected expert outputs (+ optional residual)
+// and the unit-gain RMSNorm of the decoder block.
 //
-// Combine: y = w_1 E_{i1}(x) + w_2 E_{i2}(x) (Mixtral of Experts, paper-graph-ui
-// page, section 3.4, output equation), summed in fp32 in slot order; the
+// Combine: y = sum_s w_s E_{i_s}(x) (Mixtral of Experts, paper-graph-ui page,
+// section 3.4, output equation; two terms in Mixtral), summed in fp32 in slot order; the
 // residual-stream add (section 3.2) comes after, then one rounding.
 // RMSNorm: x = h / sqrt(mean(h^2) + eps) (section 3.4, "Architectural
 // Inheritance from Mistral 7B", layer normalization; unit gain).
@@ -15,34 +15,37 @@ namespace moe {
 
 namespace {
 
-template <bool BF16>
+template <bool BF16, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ residual, void* y,
                                                       int d, const float* __restrict__ y_perm_hi) {
     const int t = blockIdx.x;
-    const int r0 = row_of[2 * t], r1 = row_of[2 * t + 1];
-    const float g0 = gate[2 * t], g1 = gate[2 * t + 1];
-    const float4* p0 = reinterpret_cast<const float4*>(y_perm + static_cast<size_t>(r0 < 0 ? 0 : r0) * d);
-    const float4* p1 = reinterpret_cast<const float4*>(y_perm + static_cast<size_t>(r1 < 0 ? 0 : r1) * d);
+    int r[K];
+    float g[K];
+    const float4* p[K];
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        r[s] = row_of[K * t + s];
+        g[s] = gate[K * t + s];
+        p[s] = reinterpret_cast<const float4*>(y_perm + static_cast<size_t>(r[s] < 0 ? 0 : r[s]) * d);
+    }
     for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
         float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r0 >= 0) {
-            float4 a = p0[c];
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            if (r[s] < 0) continue;
+            float4 a = p[s][c];
             if (y_perm_hi != nullptr) {
-                const float4 a2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r0) * d)[c];
+                const float4 a2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r[s]) * d)[c];
                 a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
             }
-            v[0] = g0 * a.x; v[1] = g0 * a.y; v[2] = g0 * a.z; v[3] = g0 * a.w;
-        }
-        if (r1 >= 0) {
-            float4 b = p1[c];
-            if (y_perm_hi != nullptr) {
-                const float4 b2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r1) * d)[c];
-                b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+            if (s == 0) {
+                v[0] = g[s] * a.x; v[1] = g[s] * a.y; v[2] = g[s] * a.z; v[3] = g[s] * a.w;
+            } else {
+                v[0] += g[s] * a.x; v[1] += g[s] * a.y; v[2] += g[s] * a.z; v[3] += g[s] * a.w;
             }
-            v[0] += g1 * b.x; v[1] += g1 * b.y; v[2] += g1 * b.z; v[3] += g1 * b.w;
         }
         const size_t o = static_cast<size_t>(t) * d + 4 * c;
         if (BF16) {
@@ -112,13 +115,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
 
 }  // namespace
 
+template <bool BF16>
+static void combine_k(const Shape& s, const float* y_perm, const int32_t* row_of, const float* gate,
+                      const void* residual, void* y, hipStream_t st, const float* y_perm_hi) {
+    switch (s.K) {
+        case 1: combine_kernel<BF16, 1><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 2: combine_kernel<BF16, 2><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 3: combine_kernel<BF16, 3><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        default: combine_kernel<BF16, 4><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+    }
+}
+
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
                           const float* gate, const void* residual, void* y, hipStream_t st,
                           const float* y_perm_hi) {
+    static_assert(kMaxTopK == 4, "one combine instance per K");
+    if (s.K < 1 || s.K > kMaxTopK) return hipErrorInvalidValue;
     if (s.bf16)
-        combine_kernel<true><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi);
+        combine_k<true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
     else
-        combine_kernel<false><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi);
+        combine_k<false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
     return hipGetLastError();
 }
 

@@ -28,17 +28,14 @@ namespace moe {
 
 namespace {
 
-constexpr int kExperts = 8;
-
 // ---------------------------------------------------------------------------
 // Helpers
 // ---------------------------------------------------------------------------
 
 // Expert owning permuted row p (segments are laid out in expert order).
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int p) {
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int n_exp, int p) {
     int e = 0;
-#pragma unroll
-    for (int j = 1; j < kExperts; ++j) e = (p >= offsets[j]) ? j : e;
+    for (int j = 1; j < n_exp; ++j) e = (p >= offsets[j]) ? j : e;
     return e;
 }
 
@@ -166,7 +163,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
-    int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P) {
+    int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P, int topk) {
     // Two stage buffers (each 4 wave slices of 8 KB); after the K loop they
     // hold the cross-wave reduction [wave][token block][weight block][lane].
     __shared__ uint4 sb0[4 * kStreamWaveVec];
@@ -218,7 +215,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
         const bf16_t* arow[kStreamMaxTB];
         uint32_t amask[kStreamMaxTB];
         const int src0 = DUAL ? row_src[seg] : 0;
-        const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? (src0 >> 1) : 0) : seg;
+        const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? static_cast<int>(static_cast<uint32_t>(src0) / static_cast<uint32_t>(topk)) : 0) : seg;
 #pragma unroll
         for (int tb = 0; tb < kStreamMaxTB; ++tb) {
             const int p = seg + (tb0 + tb) * 16 + r;
@@ -228,7 +225,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 if (DUAL) {
                     const int src = row_src[p];
                     real = src >= 0 && src < n_src;
-                    if (real) row = src >> 1;
+                    if (real) row = static_cast<int>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk));
                 } else {
                     real = true;
                     row = p;
@@ -313,14 +310,14 @@ __global__ __launch_bounds__(256) void f32_kernel(
     const float* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const float* __restrict__ wa, const float* __restrict__ wb, float* __restrict__ out,
-    int Kdim, int Nw, int ld_act, int n_src, int P) {
+    int Kdim, int Nw, int ld_act, int n_src, int P, int n_exp, int topk) {
     __shared__ float sa[16][33];
     __shared__ float s1[64][33];
     __shared__ float s3[DUAL ? 64 : 1][33];
 
     const int p0 = blockIdx.x * 16;
-    if (p0 >= offsets[kExperts]) return;
-    const int e = expert_of_row(offsets, p0);
+    if (p0 >= offsets[n_exp]) return;
+    const int e = expert_of_row(offsets, n_exp, p0);
     const int row_end = min(offsets[e + 1], P);
     const int valid = min(min(16, offsets[e] + counts[e] - p0), row_end - p0);
     if (valid <= 0) return;
@@ -335,7 +332,7 @@ __global__ __launch_bounds__(256) void f32_kernel(
         if (rr < valid) {
             if (DUAL) {
                 const int src = row_src[p0 + rr];
-                if (src >= 0 && src < n_src) arow = act + static_cast<size_t>(src >> 1) * ld_act;
+                if (src >= 0 && src < n_src) arow = act + static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act;
             } else {
                 arow = act + static_cast<size_t>(p0 + rr) * ld_act;
             }
@@ -407,13 +404,13 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
                                                offsets, static_cast<const float*>(w1),
                                                static_cast<const float*>(w3),
                                                static_cast<float*>(h), s.d, s.F, s.d, s.T * s.K,
-                                               pmax_rows(s, 16));
+                                               pmax_rows(s, 16), s.n, s.K);
     } else if (tile_m == 16) {
         dim3 grid(s.F / 32, s.n);
         stream_kernel<true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts,
                                                   offsets, static_cast<const bf16_t*>(w1),
                                                   static_cast<const bf16_t*>(w3), h, s.d, s.F, s.d,
-                                                  s.T * s.K, pmax_rows(s, 16));
+                                                  s.T * s.K, pmax_rows(s, 16), s.K);
     } else {
         return launch_tiled(s, true, x, row_src, counts, offsets, w1, w3, h, st);
     }
@@ -429,13 +426,13 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
         f32_kernel<false><<<grid, 256, 0, st>>>(static_cast<const float*>(h), nullptr, counts,
                                                 offsets, static_cast<const float*>(w2), nullptr,
                                                 y_perm, s.F, s.d, s.F, s.T * s.K,
-                                                pmax_rows(s, 16));
+                                                pmax_rows(s, 16), s.n, s.K);
     } else if (tile_m == 16) {
         dim3 grid(s.d / 64, s.n);
         stream_kernel<false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts,
                                                    offsets, static_cast<const bf16_t*>(w2), nullptr,
                                                    y_perm, s.F, s.d, s.F, s.T * s.K,
-                                                pmax_rows(s, 16));
+                                                   pmax_rows(s, 16), s.K);
     } else {
         int ks = 1;
         if (y_perm_hi != nullptr) {

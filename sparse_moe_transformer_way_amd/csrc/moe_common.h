@@ -61,8 +61,12 @@ __device__ __forceinline__ float silu_f32(float z) {
 // Internal launchers (host side).  Each enqueues on `stream` and returns the
 // hipGetLastError() status of its launches.  Shapes are validated by the ABI.
 // ---------------------------------------------------------------------------
+// Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
+constexpr int kMaxExperts = 16;
+constexpr int kMaxTopK = 4;
+
 struct Shape {
-    int T, d, F, n, K;
+    int T, d, F, n, K;  // n <= kMaxExperts, K <= min(n, kMaxTopK)
     bool bf16;
 };
 

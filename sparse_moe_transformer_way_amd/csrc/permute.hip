@@ -17,19 +17,20 @@ namespace moe {
 
 namespace {
 
-constexpr int kExperts = 8;
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int TK,
+// NE expert slots; experts 0..n-1 are real, any other index is ignored.
+template <int NE>
+__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int TK, int n,
                                                            int tile_m, int P_max,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ row_src,
                                                            int32_t* __restrict__ row_of) {
-    __shared__ int s_wave[kWaves][kExperts];
-    __shared__ int s_total[kExperts];
-    __shared__ int s_off[kExperts + 1];
+    __shared__ int s_wave[kWaves][NE];
+    __shared__ int s_total[NE];
+    __shared__ int s_off[NE + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -38,19 +39,19 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     const int a0 = min(TK, tid * per);
     const int a1 = min(TK, a0 + per);
 
-    int c[kExperts];
+    int c[NE];
 #pragma unroll
-    for (int e = 0; e < kExperts; ++e) c[e] = 0;
+    for (int e = 0; e < NE; ++e) c[e] = 0;
     for (int a = a0; a < a1; ++a) {
         const int e = idx[a];
 #pragma unroll
-        for (int j = 0; j < kExperts; ++j) c[j] += (e == j) ? 1 : 0;
+        for (int j = 0; j < NE; ++j) c[j] += (e == j && j < n) ? 1 : 0;
     }
 
     // Inclusive scan of each expert's count across the wave.
-    int incl[kExperts];
+    int incl[NE];
 #pragma unroll
-    for (int e = 0; e < kExperts; ++e) {
+    for (int e = 0; e < NE; ++e) {
         int v = c[e];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -61,10 +62,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     }
     if (lane == 63) {
 #pragma unroll
-        for (int e = 0; e < kExperts; ++e) s_wave[wave][e] = incl[e];
+        for (int e = 0; e < NE; ++e) s_wave[wave][e] = incl[e];
     }
     __syncthreads();
-    if (tid < kExperts) {
+    if (tid < NE) {
         int run = 0;
         for (int w = 0; w < kWaves; ++w) {
             const int v = s_wave[w][tid];
@@ -76,26 +77,28 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     __syncthreads();
     if (tid == 0) {
         int off = 0;
-        for (int e = 0; e < kExperts; ++e) {
+        for (int e = 0; e < NE; ++e) {
             s_off[e] = off;
-            counts[e] = s_total[e];
-            offsets[e] = off;
-            off += (s_total[e] + tile_m - 1) / tile_m * tile_m;
+            if (e < n) {
+                counts[e] = s_total[e];
+                offsets[e] = off;
+            }
+            off += (s_total[e] + tile_m - 1) / tile_m * tile_m;  // zero past n
         }
-        s_off[kExperts] = off;
-        offsets[kExperts] = off;
+        s_off[NE] = off;
+        offsets[n] = off;
     }
     __syncthreads();
 
-    int pos[kExperts];
+    int pos[NE];
 #pragma unroll
-    for (int e = 0; e < kExperts; ++e) pos[e] = s_off[e] + s_wave[wave][e] + incl[e] - c[e];
+    for (int e = 0; e < NE; ++e) pos[e] = s_off[e] + s_wave[wave][e] + incl[e] - c[e];
     for (int a = a0; a < a1; ++a) {
         const int e = idx[a];
         int p = -1;
 #pragma unroll
-        for (int j = 0; j < kExperts; ++j) {
-            if (e == j) {
+        for (int j = 0; j < NE; ++j) {
+            if (e == j && j < n) {
                 p = pos[j];
                 pos[j] = p + 1;
             }
@@ -105,12 +108,12 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     }
 
     // Padding rows of every segment, then everything past the last segment.
-    for (int e = 0; e < kExperts; ++e) {
+    for (int e = 0; e < n; ++e) {
         const int lo = s_off[e] + s_total[e];
         const int hi = s_off[e + 1];
         for (int p = lo + tid; p < hi; p += kThreads) row_src[p] = -1;
     }
-    for (int p = s_off[kExperts] + tid; p < P_max; p += kThreads) row_src[p] = -1;
+    for (int p = s_off[NE] + tid; p < P_max; p += kThreads) row_src[p] = -1;
 }
 
 }  // namespace
@@ -119,7 +122,10 @@ hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_
                           int32_t* offsets, int32_t* row_src, int32_t* row_of, hipStream_t st) {
     const int TK = s.T * s.K;
     const int P_max = TK + s.n * (tile_m - 1);
-    permute_kernel<<<1, kThreads, 0, st>>>(idx, TK, tile_m, P_max, counts, offsets, row_src, row_of);
+    if (s.n <= 8)
+        permute_kernel<8><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
+    else
+        permute_kernel<16><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
     return hipGetLastError();
 }
 

@@ -1,13 +1,13 @@
-// Router: logits l = x . W_g (fp32), Top-2 with ties to the lower expert index,
-// and the softmax over the two survivors.
+// Router: logits l = x . W_g (fp32), Top-K with ties to the lower expert index,
+// and the softmax over the K survivors.
 //
 // Mixtral of Experts, paper-graph-ui page, section 3.4 "MoE Layer Formulation"
 // (G(x) = Softmax(TopK(x . W_g)), TopK sets the non-selected logits to -inf) and
-// "Top-K Gating Mechanism and Routing" (no bias; pick the two largest, mask,
-// softmax).  Softmax of a vector whose other entries are -inf reduces to the
-// two-term form g0 = 1/(1+e), g1 = e/(1+e), e = exp(l_second - l_first).
+// "Top-K Gating Mechanism and Routing" (no bias; pick the largest, mask,
+// softmax; Mixtral takes K = 2 of n = 8).  Softmax of a vector whose other
+// entries are -inf reduces to the K-term form over the survivors only.
 //
-// Layout: a block of 4 waves handles TOK tokens (8, or 1 for small batches so
+// Layout: a block of 4 waves handles TOK tokens (8, 4 with 16 expert slots, or 1 for small batches so
 // that a decode step still spreads over T blocks); the d channels are cut into
 // 8-channel chunks and wave w takes the w-th quarter of the chunks, so a token's
 // dot products are spread over 256 lanes (few sequential steps even at decode
@@ -17,48 +17,66 @@
 // per lane.  Per-lane partial sums go through an xor butterfly inside the wave,
 // then the 4 wave sums are added in wave order through LDS (a fixed order, so
 // the logits are deterministic), and lane t of wave 0 finishes token t.
+// NE is the compile-time expert slot count (8 or 16); W_g takes the vector
+// path when n == NE and a scalar one otherwise.
 #include "moe_common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kExperts = 8;
 constexpr int kWaves = 4;         // waves per block, splitting d
 constexpr int kSmallT = 256;      // up to this many tokens: one token per block
 
-template <bool BF16, int kTok>
+// Whether (v, i) comes before (w, j) in the order key (logit descending, then
+// expert index ascending); j < 0 marks an empty slot.
+__device__ __forceinline__ bool before(float v, int i, float w, int j) {
+    return j < 0 || v > w || (v == w && i < j);
+}
+
+// TOK tokens per block, NE = expert slots (n <= NE experts are real).
+template <bool BF16, int TOK, int NE>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ xv,
-                                                          const float* __restrict__ wg, int T,
-                                                          int d, int32_t* __restrict__ idx,
+                                                          const float* __restrict__ wg, int T, int d, int n,
+                                                          int K, int32_t* __restrict__ idx,
                                                           float* __restrict__ gate,
                                                           float* __restrict__ logits) {
-    __shared__ float part[kWaves][kTok][kExperts];
+    __shared__ float part[kWaves][TOK][NE];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kTok;
+    const int t0 = blockIdx.x * TOK;
     const int nch = d >> 3;
     const int cbeg = wave * nch / kWaves;
     const int cend = (wave + 1) * nch / kWaves;
+    const bool full = n == NE;  // W_g rows are NE floats: vector loads
 
-    float acc[kTok][kExperts];
+    float acc[TOK][NE];
 #pragma unroll
-    for (int t = 0; t < kTok; ++t)
+    for (int t = 0; t < TOK; ++t)
 #pragma unroll
-        for (int e = 0; e < kExperts; ++e) acc[t][e] = 0.0f;
+        for (int e = 0; e < NE; ++e) acc[t][e] = 0.0f;
 
     for (int ch = cbeg + lane; ch < cend; ch += 64) {
         const int k0 = ch * 8;
-        float w[8][kExperts];
-        const float4* wp = reinterpret_cast<const float4*>(wg + static_cast<size_t>(k0) * kExperts);
+        float w[8][NE];
+        if (full) {
+            const float4* wp = reinterpret_cast<const float4*>(wg + static_cast<size_t>(k0) * NE);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float4 a = wp[2 * j], b = wp[2 * j + 1];
-            w[j][0] = a.x; w[j][1] = a.y; w[j][2] = a.z; w[j][3] = a.w;
-            w[j][4] = b.x; w[j][5] = b.y; w[j][6] = b.z; w[j][7] = b.w;
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int q = 0; q < NE / 4; ++q) {
+                    const float4 a = wp[j * (NE / 4) + q];
+                    w[j][4 * q] = a.x; w[j][4 * q + 1] = a.y; w[j][4 * q + 2] = a.z; w[j][4 * q + 3] = a.w;
+                }
+        } else {
+            const float* wr = wg + static_cast<size_t>(k0) * n;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < NE; ++e) w[j][e] = e < n ? wr[j * n + e] : 0.0f;
         }
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
+        for (int t = 0; t < TOK; ++t) {
             if (t0 + t < T) {
                 float xf[8];
                 if (BF16) {
@@ -74,15 +92,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
 #pragma unroll
-                    for (int e = 0; e < kExperts; ++e) acc[t][e] = fmaf(xf[j], w[j][e], acc[t][e]);
+                    for (int e = 0; e < NE; ++e) acc[t][e] = fmaf(xf[j], w[j][e], acc[t][e]);
             }
         }
     }
 
 #pragma unroll
-    for (int t = 0; t < kTok; ++t)
+    for (int t = 0; t < TOK; ++t)
 #pragma unroll
-        for (int e = 0; e < kExperts; ++e) {
+        for (int e = 0; e < NE; ++e) {
             float v = acc[t][e];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -90,62 +108,96 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
         }
     if (lane == 0) {
 #pragma unroll
-        for (int t = 0; t < kTok; ++t)
+        for (int t = 0; t < TOK; ++t)
 #pragma unroll
-            for (int e = 0; e < kExperts; ++e) part[wave][t][e] = acc[t][e];
+            for (int e = 0; e < NE; ++e) part[wave][t][e] = acc[t][e];
     }
     __syncthreads();
-    if (wave != 0 || lane >= kTok) return;
+    if (wave != 0 || lane >= TOK) return;
     const int t = lane;
     const int tok = t0 + t;
     if (tok >= T) return;
-    float l[kExperts];
+    float l[NE];
 #pragma unroll
-    for (int e = 0; e < kExperts; ++e)
+    for (int e = 0; e < NE; ++e)
         l[e] = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
-    // Order key (logit descending, index ascending): strict '>' keeps the
-    // earlier (lower) index on equality.
-    int i0 = 0, i1 = -1;
-    float v0 = l[0], v1 = -INFINITY;
+    // Top-K by the order key: each expert, in index order, is bubbled into the
+    // sorted slots; a displaced entry moves down with a full key comparison.
+    int ix[kMaxTopK];
+    float vx[kMaxTopK];
 #pragma unroll
-    for (int e = 1; e < kExperts; ++e) {
-        const float v = l[e];
-        if (v > v0) {
-            i1 = i0; v1 = v0; i0 = e; v0 = v;
-        } else if (v > v1 || i1 < 0) {
-            i1 = e; v1 = v;
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ix[s] = -1;
+        vx[s] = -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        float v = l[e];
+        int i = e;
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (e < n && s < K && before(v, i, vx[s], ix[s])) {
+                const float tv = vx[s];
+                const int ti = ix[s];
+                vx[s] = v;
+                ix[s] = i;
+                v = tv;
+                i = ti;
+            }
         }
     }
-    const float ex = expf(v1 - v0);
-    const float sum = 1.0f + ex;
-    idx[2 * tok] = i0;
-    idx[2 * tok + 1] = i1;
-    gate[2 * tok] = 1.0f / sum;
-    gate[2 * tok + 1] = ex / sum;
-    if (logits != nullptr) {
-        float4* lp = reinterpret_cast<float4*>(logits + static_cast<size_t>(tok) * kExperts);
-        lp[0] = make_float4(l[0], l[1], l[2], l[3]);
-        lp[1] = make_float4(l[4], l[5], l[6], l[7]);
+    // Softmax over the K survivors (the others are -inf): e_s = exp(l_s - l_0),
+    // g_s = e_s / sum_j e_j, summed in slot order.  For K = 2 this is
+    // g0 = 1 / (1 + e), g1 = e / (1 + e) with e = exp(l_1 - l_0).
+    float ex[kMaxTopK];
+    float sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ex[s] = s == 0 ? 1.0f : (s < K ? expf(vx[s] - vx[0]) : 0.0f);
+        if (s < K) sum += ex[s];
     }
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s < K) {
+            idx[static_cast<size_t>(tok) * K + s] = ix[s];
+            gate[static_cast<size_t>(tok) * K + s] = ex[s] / sum;
+        }
+    }
+    if (logits != nullptr) {
+        float* lp = logits + static_cast<size_t>(tok) * n;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (e < n) lp[e] = l[e];
+    }
+}
+
+template <int TOK, int NE>
+void launch_router(const Shape& s, const void* x, const float* wg, int32_t* idx, float* gate, float* logits,
+                   hipStream_t st) {
+    const int blocks = (s.T + TOK - 1) / TOK;
+    if (s.bf16)
+        router_topk_kernel<true, TOK, NE><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, s.n, s.K, idx, gate, logits);
+    else
+        router_topk_kernel<false, TOK, NE><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, s.n, s.K, idx, gate, logits);
 }
 
 }  // namespace
 
 hipError_t launch_router_topk(const Shape& s, const void* x, const float* wg, int32_t* idx,
                               float* gate, float* logits, hipStream_t st) {
-    // Each block reads all of W_g (d x 8 fp32, from L2): one token per block
-    // for small batches, eight when W_g reuse matters more than parallelism.
-    if (s.T <= kSmallT) {
-        if (s.bf16)
-            router_topk_kernel<true, 1><<<s.T, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+    // Each block reads all of W_g (d x n fp32, from L2): one token per block
+    // for small batches, several when W_g reuse matters more than parallelism.
+    const bool small = s.T <= kSmallT;
+    if (s.n <= 8) {
+        if (small)
+            launch_router<1, 8>(s, x, wg, idx, gate, logits, st);
         else
-            router_topk_kernel<false, 1><<<s.T, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+            launch_router<8, 8>(s, x, wg, idx, gate, logits, st);
     } else {
-        const int blocks = (s.T + 7) / 8;
-        if (s.bf16)
-            router_topk_kernel<true, 8><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+        if (small)
+            launch_router<1, 16>(s, x, wg, idx, gate, logits, st);
         else
-            router_topk_kernel<false, 8><<<blocks, 256, 0, st>>>(x, wg, s.T, s.d, idx, gate, logits);
+            launch_router<4, 16>(s, x, wg, idx, gate, logits, st);
     }
     return hipGetLastError();
 }

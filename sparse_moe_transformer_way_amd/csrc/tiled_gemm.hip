@@ -56,7 +56,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kExperts = 8;
 constexpr int kTW = 256;                     // weight rows per tile
 constexpr int kTT = 256;                     // token rows per tile
 constexpr int kBK = 64;                      // k per LDS buffer (one "block")
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_wt,
-    int ld_out, int n_src, int P, int ksplit, size_t split_stride) {
+    int ld_out, int n_src, int P, int ksplit, size_t split_stride, int n_exp, int topk) {
     __shared__ uint4 b0[kBufVec];
     __shared__ uint4 b1[kBufVec];
 
@@ -228,8 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // evenly: XCD x (workgroups b with b % 8 == x) takes a contiguous run of
     // ceil(total / 8) of them, and the remaining workgroups exit here.
     int per_split = 0;
-#pragma unroll
-    for (int j = 0; j < kExperts; ++j) per_split += (offsets[j + 1] - offsets[j]) / kTT * n_wt;
+    for (int j = 0; j < n_exp; ++j) per_split += (offsets[j + 1] - offsets[j]) / kTT * n_wt;
     const int total = per_split * ksplit;
     const int run = (total + 7) >> 3;
     if (static_cast<int>(blockIdx.x >> 3) >= run) return;
@@ -242,12 +240,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     out = static_cast<char*>(out) + split * split_stride * (DUAL ? sizeof(bf16_t) : sizeof(float));
     // expert e owns tiles [sum of earlier experts' n_tt_e * n_wt, + n_tt_e * n_wt)
     int e = 0, ntt_e = 0;
-    for (; e < kExperts; ++e) {
+    for (; e < n_exp; ++e) {
         ntt_e = (offsets[e + 1] - offsets[e]) / kTT;  // segments are padded to kTT rows
         if (L < ntt_e * n_wt) break;
         L -= ntt_e * n_wt;
     }
-    if (e == kExperts) return;
+    if (e == n_exp) return;
     // groups of gn weight tiles x the expert's ntt_e token tiles, token-major
     const int gn = max(1, min(n_wt, kXcdTiles / ntt_e));
     const int g = L / (gn * ntt_e);
@@ -297,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (src < 0 || src >= n_src) src = first_src;
                 if (src < 0 || src >= n_src) src = 0;
                 c.to[j] = static_cast<uint32_t>(
-                    (static_cast<size_t>(src >> 1) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
+                    (static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
             }
             c.tstride = 0;
         } else {
@@ -412,11 +410,11 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
                                               static_cast<const bf16_t*>(wa), static_cast<const bf16_t*>(wb),
                                               out, s.d, s.F, s.d, n_wt, s.F, s.T * s.K, P,
-                                              ksplit, split_stride);
+                                              ksplit, split_stride, s.n, s.K);
     else
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
-                                               n_wt, s.d, s.T * s.K, P, ksplit, split_stride);
+                                               n_wt, s.d, s.T * s.K, P, ksplit, split_stride, s.n, s.K);
     return hipGetLastError();
 }
 

@@ -67,7 +67,13 @@ def test_sizes():
     ws = moe.moe_workspace_size(d, 4096, 0)
     P = 8192 + 8 * 255
     assert ws >= P * 14336 * 2 + P * 4096 * 4
-    assert moe.moe_workspace_size(D(n_experts=4), 10, 0) == 0
+    # 1 <= K <= n, n <= 16, K <= 4
+    assert moe.moe_workspace_size(D(n_experts=17), 10, 0) == 0
+    assert moe.moe_workspace_size(D(n_experts=16, top_k=5), 10, 0) == 0
+    assert moe.moe_workspace_size(D(n_experts=3, top_k=4), 10, 0) == 0
+    for n, K in [(16, 4), (4, 1), (1, 1), (5, 3)]:
+        assert moe.moe_workspace_size(D(n_experts=n, top_k=K), 10, 0) > 0
+        assert moe.moe_max_permuted_rows(D(n_experts=n, top_k=K), 10, 16) == 10 * K + n * 15
     assert moe.moe_block_workspace_size(d, 100) > moe.moe_workspace_size(d, 100, 0)
 
 
@@ -76,9 +82,10 @@ FAKE = 0x100000  # 16-byte-aligned non-null pointer value; never dereferenced
 
 @pytest.mark.parametrize("desc,T,expect", [
     (None, 4, 1),
-    (D(n_experts=4), 4, 2),
-    (D(top_k=1), 4, 2),
+    (D(n_experts=17), 4, 2),
+    (D(top_k=5), 4, 2),
     (D(top_k=9), 4, 1),
+    (D(top_k=0), 4, 1),
     (D(act_dtype=0), 4, 2),
     (D(act_dtype=7), 4, 1),
     (D(d_model=100), 4, 1),

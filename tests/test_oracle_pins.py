@@ -115,6 +115,8 @@ def test_routing_margin_hand():
     x, wg, *_ = hand_example()
     np.testing.assert_array_equal(oracle.routing_margin(x, wg), [0.5, 0.0])
     np.testing.assert_array_equal(oracle.top_gap(x, wg), [0.5, 1.0])
+    np.testing.assert_array_equal(oracle.slot_order_gap(x, wg, 2), [0.5, 1.0])
+    assert np.isinf(oracle.slot_order_gap(x, wg, 1)).all()
 
 
 # ---------------------------------------------------------------------------
@@ -126,21 +128,43 @@ def _key_beats(l, i, j):
     return l[i] > l[j] or (l[i] == l[j] and i < j)
 
 
+@pytest.mark.parametrize("n,K", [(8, 2), (4, 1), (8, 3), (8, 4), (16, 2), (16, 4), (5, 5)])
 @pytest.mark.parametrize("grid", [None, 1.0, 0.25])
-def test_top2_brute_force(grid):
-    rng = np.random.default_rng(123)
-    n = 8
-    logits = rng.standard_normal((400, n)).astype(np.float32)
+def test_topk_brute_force(n, K, grid):
+    """Every K-subset is tried: exactly one beats all unselected experts under
+    the (logit desc, index asc) key, and the oracle returns it in key order."""
+    rng = np.random.default_rng(123 + 16 * n + K)
+    logits = rng.standard_normal((150, n)).astype(np.float32)
     if grid is not None:  # coarse grid -> many exact ties
         logits = (np.round(logits / grid) * grid).astype(np.float32)
-    idx = oracle.topk_indices(logits, 2)
+    idx = oracle.topk_indices(logits, K)
     for t in range(logits.shape[0]):
         l = logits[t]
-        winners = [pair for pair in itertools.combinations(range(n), 2)
-                   if all(_key_beats(l, a, b) for a in pair for b in range(n) if b not in pair)]
+        winners = [sub for sub in itertools.combinations(range(n), K)
+                   if all(_key_beats(l, a, b) for a in sub for b in range(n) if b not in sub)]
         assert len(winners) == 1
         assert set(idx[t]) == set(winners[0])
-        assert _key_beats(l, idx[t, 0], idx[t, 1])
+        for s in range(K - 1):
+            assert _key_beats(l, idx[t, s], idx[t, s + 1])
+
+
+def test_top1_gate_is_one():
+    """K = 1: the softmax over one surviving logit is exactly 1."""
+    inp = mi.make_layer(64, 32, 16, n=6, K=1, dtype="f32", init="fanin", seed=8, workload=103)
+    x, wg, *_ = inp.numpy_f32()
+    G, idx, l = oracle.gating(x, wg, K=1)
+    rows = np.arange(64)
+    assert (G[rows, idx[:, 0]] == 1.0).all() and ((G != 0).sum(axis=1) == 1).all()
+    np.testing.assert_array_equal(idx[:, 0], np.argmax(l, axis=1))
+
+
+def test_topk_all_experts_is_plain_softmax():
+    """K = n: TopK masks nothing, so G is the textbook softmax of the logits."""
+    from scipy.special import softmax as sp_softmax
+    inp = mi.make_layer(50, 32, 16, n=5, K=5, dtype="f32", init="fanin", seed=9, workload=104)
+    x, wg, *_ = inp.numpy_f32()
+    G, _, l = oracle.gating(x, wg, K=5)
+    np.testing.assert_allclose(G, sp_softmax(np.asarray(l, np.float64), axis=1), rtol=2e-6, atol=1e-7)
 
 
 def test_top2_scale_invariance():
@@ -258,10 +282,11 @@ def test_fp64_loop_bound():
 # Reference layouts
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("n,K", [(8, 2), (16, 4), (3, 1), (6, 3)])
 @pytest.mark.parametrize("tile_m", [1, 16, 128])
-def test_group_by_expert_properties(tile_m):
-    rng = np.random.default_rng(tile_m)
-    T, K, n = 300, 2, 8
+def test_group_by_expert_properties(tile_m, n, K):
+    rng = np.random.default_rng(tile_m + 100 * n + K)
+    T = 300
     idx = np.stack([rng.permutation(n)[:K] for _ in range(T)]).astype(np.int32)
     g = oracle.group_by_expert(idx, n, tile_m)
     counts, offsets, row_src, row_of = g["counts"], g["offsets"], g["row_src"], g["row_of"]
@@ -286,6 +311,20 @@ def test_sparse_path_equals_dense():
     out = oracle.moe_layer(x, wg, w1, w3, w2)
     g = oracle.group_by_expert(out["idx"], 8, 16)
     _, y_perm = oracle.expert_rows(x, g["row_src"], g["offsets"], w1, w3, w2)
+    y = oracle.combine(y_perm, g["row_of"], out["gates"])
+    np.testing.assert_allclose(y, out["y"], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("n,K", [(6, 3), (16, 4), (4, 1)])
+def test_sparse_path_equals_dense_general_k(n, K):
+    """Grouped rows + slot-order combine reproduce the dense per-token sum for
+    other expert counts and K (token of assignment a is a // K)."""
+    inp = mi.make_layer(40, 32, 24, n=n, K=K, dtype="f32", init="fanin", seed=n + K, workload=105)
+    x, wg, w1, w3, w2 = inp.numpy_f32()
+    out = oracle.moe_layer(x, wg, w1, w3, w2, K=K)
+    assert out["idx"].shape == (40, K)
+    g = oracle.group_by_expert(out["idx"], n, 16)
+    _, y_perm = oracle.expert_rows(x, g["row_src"], g["offsets"], w1, w3, w2, K=K)
     y = oracle.combine(y_perm, g["row_of"], out["gates"])
     np.testing.assert_allclose(y, out["y"], rtol=1e-5, atol=1e-6)
 
