@@ -8,3 +8,6 @@ from .moe_oracle import (  # noqa: F401
     moe_layer, rmsnorm, round_bf16, moe_block, max_permuted_rows, group_by_expert,
     expert_rows, combine, routing_margin, top_gap, slot_order_gap,
 )
+from .fp8 import (  # noqa: F401
+    e4m3_decode, e4m3_encode_rne, quantize_rows_fp8, dequantize_rows_fp8, moe_layer_fp8,
+)

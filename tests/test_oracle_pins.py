@@ -388,3 +388,86 @@ def test_tiny_workload_runs_fast():
     inp = mi.make_workload(0)
     out = oracle.moe_layer(*inp.numpy_f32())
     assert out["y"].shape == (64, 128) and out["counts"].sum() == 128
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) expert weights
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_all_codes_vs_torch():
+    """Every code against torch's float8_e4m3fn (a library decoder)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert ((got == ref) | (np.isnan(got) & np.isnan(ref))).all()
+    assert np.isnan(got).sum() == 2  # 0x7F and 0xFF
+
+
+def test_e4m3_hand_values():
+    d = oracle.e4m3_decode(np.array([0x38, 0x3C, 0x7E, 0x01, 0x07, 0x08, 0x80, 0x00, 0xB8, 0x7F], np.uint8))
+    np.testing.assert_array_equal(d[:8], [1.0, 1.5, 448.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 0.0, 0.0])
+    assert np.signbit(d[6]) and not np.signbit(d[7])
+    assert d[8] == -1.0 and np.isnan(d[9])
+
+
+def test_e4m3_encode_vs_torch_in_range():
+    """Inside +-448 the oracle's rounding equals torch's round-to-nearest-even
+    cast, on random values over many binades and on every exact midpoint
+    between neighbouring codes (ties go to the even mantissa)."""
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(50000) * rng.choice([1e-3, 0.05, 1.0, 100.0], 50000)).astype(np.float32)
+    v = np.clip(v, -448, 448).astype(np.float32)
+    vals = np.unique(oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert (mids.astype(np.float64) == (vals[:-1] + vals[1:]) / 2).all()  # exact in fp32
+    for a in (v, mids, -mids):
+        ref = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(oracle.e4m3_encode_rne(a), ref)
+    # a tie between 1.0 (M=0) and 1.125 (M=1) goes to 1.0; between 1.125 and 1.25 to 1.25
+    np.testing.assert_array_equal(oracle.e4m3_encode_rne(np.array([1.0625, 1.1875], np.float32)), [0x38, 0x3A])
+
+
+def test_e4m3_saturation():
+    got = oracle.e4m3_encode_rne(np.array([448, 449, 500, 1e30, -1e30, -460], np.float32))
+    np.testing.assert_array_equal(got, [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+
+
+def test_quantize_rows_bounds():
+    """Round trip within half a quantum of w / scale; every non-zero row
+    reaches the code of +-448; an all-zero row gets scale 1 and code 0."""
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((3, 40, 96)) * 0.02).astype(np.float32)
+    w[1, 5] = 0.0
+    q, s = oracle.quantize_rows_fp8(w)
+    assert q.shape == w.shape and s.shape == (3, 40) and s.dtype == np.float32
+    assert s[1, 5] == 1.0 and (q[1, 5] == 0).all()
+    v = (w / s[..., None]).astype(np.float64)
+    dq = oracle.e4m3_decode(q)
+    a = np.abs(v)
+    half_quantum = np.where(a >= 2.0 ** -6, np.ldexp(1.0, np.frexp(a)[1] - 1 - 4), 2.0 ** -10)
+    assert (np.abs(dq - v) <= half_quantum).all()
+    nz = np.abs(w).max(axis=-1) > 0
+    assert ((np.abs(dq).max(axis=-1) == 448.0) == nz).all()
+
+
+def test_fp8_layer_equals_plain_layer_on_representable_weights():
+    """Weights that are E4M3 values times a power of two, with a row maximum of
+    448 times that power, quantize without error (scale exact, codes exact), so
+    the FP8 layer must equal the plain layer bit for bit."""
+    rng = np.random.default_rng(11)
+    T, d, F, n = 24, 32, 48, 8
+    pos = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+
+    def draw(shape, m):
+        w = (rng.choice(pos, size=shape) * rng.choice([-1.0, 1.0], size=shape))
+        w[..., 0] = 448.0  # the row maximum
+        return (w * 2.0 ** -m).astype(np.float32)
+
+    w1, w3, w2 = draw((n, F, d), 12), draw((n, F, d), 11), draw((n, d, F), 13)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = (rng.standard_normal((d, n)) * 0.3).astype(np.float32)
+    (q1, s1), (q3, s3), (q2, s2) = (oracle.quantize_rows_fp8(w) for w in (w1, w3, w2))
+    assert (s1 == np.float32(2.0 ** -12)).all() and (s2 == np.float32(2.0 ** -13)).all()
+    got = oracle.moe_layer_fp8(x, wg, q1, s1, q3, s3, q2, s2)["y"]
+    ref = oracle.moe_layer(x, wg, w1, w3, w2)["y"]
+    np.testing.assert_array_equal(got, ref)
