@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer tokens/s on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny|decode_fp8]
 
 One step is one pass of the whole layer (router -> permute -> gate/up + SwiGLU ->
 down -> combine) over one batch of synthetic tokens already resident in HBM.
@@ -10,6 +10,8 @@ Phase A times K steps of moe_layer_forward between device synchronisations
 points with HIP events around each stage, recorded on the stream the kernels
 run on, which gives each kernel's average duration for the roofline figure.
 The CPU oracle is then timed on a bounded sample of the same workload.
+decode_fp8 is the decode workload with its expert weights quantized to FP8
+(E4M3, one scale per row) on the device before any timing.
 
 Prints one JSON line.  Only one GPU is used; --gpus above 1 is refused.
 """
@@ -27,14 +29,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X + % of HBM (decode) / MFMA (prefill) roofline"
-WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3}
+WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3, "decode_fp8": 1}
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_moe_transformer_way_amd", "csrc")
 # source file of each kernel the roofline can name
 KERNEL_SRC = {"gate_up_stream": "grouped_gemm.hip", "gate_up_tiled": "tiled_gemm.hip",
-              "gate_up_f32": "grouped_gemm.hip"}
+              "gate_up_f32": "grouped_gemm.hip", "gate_up_stream_fp8": "grouped_gemm.hip"}
 
 
 def parse_args():
@@ -127,7 +129,14 @@ def main():
     dt = torch.float32 if inp.dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda")
     x, wg, w1, w3, w2 = (t.to(dev) for t in (inp.x, inp.wg, inp.w1, inp.w3, inp.w2))
-    desc = moe.make_desc(d, F, n, K, dtype=dt)
+    fp8 = args.workload == "decode_fp8"
+    wl_name = spec["name"] + ("_fp8w" if fp8 else "")
+    if fp8:
+        # weights quantized once on the device, before any timing
+        (q1, s1), (q3, s3), (q2, s2) = (moe.moe_quantize_fp8(w) for w in (w1, w3, w2))
+        del w1, w3, w2
+        torch.cuda.synchronize()
+    desc = moe.make_desc(d, F, n, K, dtype=dt, weight_dtype=torch.float8_e4m3fn if fp8 else None)
     tile_m = moe.moe_default_tile_m(desc, T)
     P = moe.moe_max_permuted_rows(desc, T, tile_m)
 
@@ -145,8 +154,12 @@ def main():
     stream = torch.cuda.current_stream()
 
     def layer_step():
-        moe.moe_layer_forward(desc, x, wg, w1, w3, w2, y=y, topk_idx_out=idx, topk_gate_out=gate,
-                              counts_out=counts, workspace=ws, stream=stream)
+        if fp8:
+            moe.moe_layer_forward_fp8(desc, x, wg, q1, s1, q3, s3, q2, s2, y=y, topk_idx_out=idx,
+                                      topk_gate_out=gate, counts_out=counts, workspace=ws, stream=stream)
+        else:
+            moe.moe_layer_forward(desc, x, wg, w1, w3, w2, y=y, topk_idx_out=idx, topk_gate_out=gate,
+                                  counts_out=counts, workspace=ws, stream=stream)
 
     stages = ["router_topk", "permute", "expert_gate_up", "expert_down", "combine"]
 
@@ -156,9 +169,15 @@ def main():
         ev[1].record(stream)
         moe.moe_permute(desc, idx, tile_m, counts, offsets, row_src, row_of, stream=stream)
         ev[2].record(stream)
-        moe.moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, h, stream=stream)
+        if fp8:
+            moe.moe_expert_gate_up_fp8(desc, T, x, row_src, counts, offsets, q1, s1, q3, s3, h, stream=stream)
+        else:
+            moe.moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, h, stream=stream)
         ev[3].record(stream)
-        moe.moe_expert_down(desc, T, tile_m, h, counts, offsets, w2, y_perm, stream=stream)
+        if fp8:
+            moe.moe_expert_down_fp8(desc, T, h, counts, offsets, q2, s2, y_perm, stream=stream)
+        else:
+            moe.moe_expert_down(desc, T, tile_m, h, counts, offsets, w2, y_perm, stream=stream)
         ev[4].record(stream)
         moe.moe_combine(desc, y_perm, row_of, gate, y=y, stream=stream)
         ev[5].record(stream)
@@ -191,15 +210,20 @@ def main():
     touched = sum(1 for c in cnt if c > 0)
     TK = T * K
     esz = 2 if dt == torch.bfloat16 else 4
+    wsz = 1 if fp8 else esz                     # bytes per expert weight
+    ssz = 4 if fp8 else 0                       # bytes of scale per weight row
     # algorithmic work of the dominant kernel (gate/up + SwiGLU): per touched
-    # expert 2*F*d weights, plus the gathered rows read and h written
-    gu_bytes = touched * 2 * F * d * esz + TK * d * esz + TK * F * esz
+    # expert 2*F*d weights (and their 2*F row scales), plus the gathered rows
+    # read and h written
+    gu_bytes = touched * 2 * F * (d * wsz + ssz) + TK * d * esz + TK * F * esz
     gu_flops = 4.0 * TK * d * F
-    layer_bytes = touched * 3 * F * d * esz + 2 * T * d * esz + d * n * 4
+    layer_bytes = touched * (3 * F * d * wsz + (2 * F + d) * ssz) + 2 * T * d * esz + d * n * 4
     layer_flops = 2.0 * TK * 3 * d * F + 2.0 * T * d * n
     gu_s = stage_ms["expert_gate_up"] / 1e3
     bound = "hbm" if (T * K) / max(1, touched) < 64 else "mfma"
     kern_name = ("gate_up_stream" if tile_m == 16 else "gate_up_tiled") if dt == torch.bfloat16 else "gate_up_f32"
+    if fp8:
+        kern_name = "gate_up_stream_fp8"
     if bound == "hbm":
         achieved = gu_bytes / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -208,7 +232,7 @@ def main():
         achieved = gu_flops / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = stored_traffic(kern_name, spec["name"])
+    roof["traffic"] = stored_traffic(kern_name, wl_name)
     roof["kernel"] = kern_name
     roof["kernel_ms"] = round(stage_ms["expert_gate_up"], 4)
     roof["algorithmic_per_launch"] = gu_bytes if bound == "hbm" else gu_flops
@@ -228,8 +252,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": spec["name"], "T": T, "d_model": d, "d_ffn": F, "n_experts": n,
-                   "top_k": K, "tile_m": tile_m, "expert_counts": cnt},
+        "config": {"workload": wl_name, "T": T, "d_model": d, "d_ffn": F, "n_experts": n,
+                   "top_k": K, "tile_m": tile_m, "expert_weights": "fp8_e4m3" if fp8 else str(inp.dtype),
+                   "expert_counts": cnt},
         "roofline": roof,
         "layer": {"hbm_GBs": round(layer_bytes / layer_s / 1e9, 1),
                   "hbm_frac": round(layer_bytes / layer_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -238,7 +263,7 @@ def main():
                   "staged_ms_per_step": round(staged_ms, 4),
                   "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not fp8:  # the oracle's cost does not depend on the weight format
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, rows_cap=32 if wl <= 1 else 64)
     print(json.dumps(out), flush=True)
 

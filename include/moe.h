@@ -55,7 +55,7 @@ typedef enum {
     MOE_ERR_HIP = 4                 /* the HIP runtime reported an error at launch */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 /* Layer shape.  d_model = d, d_ffn = F, n_experts = n, top_k = K. */
 typedef struct {
@@ -63,8 +63,8 @@ typedef struct {
     int32_t d_ffn;
     int32_t n_experts;
     int32_t top_k;
-    int32_t act_dtype;     /* moe_dtype_t of x, y, h and the expert weights */
-    int32_t weight_dtype;  /* must equal act_dtype */
+    int32_t act_dtype;     /* moe_dtype_t of x, y and h: MOE_F32 or MOE_BF16 */
+    int32_t weight_dtype;  /* act_dtype, or MOE_FP8_E4M3 with bf16 activations (the _fp8 calls) */
 } moe_layer_desc_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -90,7 +90,7 @@ int64_t moe_max_permuted_rows(const moe_layer_desc_t* desc, int32_t T, int32_t t
 size_t moe_workspace_size(const moe_layer_desc_t* desc, int32_t T, int32_t tile_m);
 
 /*
- * Router: logits, Top-2 and the softmax over the two survivors.
+ * Router: logits, Top-K and the softmax over the K survivors.
  * (paper-graph-ui page 3.4: gating equation, TopK equation, and the three
  * mechanical steps under "Top-K Gating Mechanism and Routing".)
  *
@@ -209,6 +209,50 @@ moe_status_t moe_block_forward(const moe_layer_desc_t* desc, int32_t T, const vo
                                const void* w2, void* h_out, int32_t* topk_idx_out,
                                int32_t* counts_out, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * FP8 expert weights.  The pages name FP8 weights as the next serving step
+ * (paper-graph-ui page, section 3.4, "TensorRT-LLM integration" paragraph;
+ * section 6.1, "Mitigation status") but fix no format.  Here: OCP E4M3 codes
+ * (1 byte: sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals; no
+ * infinities; largest finite 448) and one fp32 scale per weight row, so that
+ * weight[r, c] = decode(code[r, c]) * scale[r].
+ *
+ * moe_quantize_fp8: per-row quantization of a bf16 matrix w [rows, cols]
+ * (cols % 8 == 0; w 16-byte and q 8-byte aligned):
+ *     scale[r]  = max_c |w[r, c]| / 448 in fp32 (1 for an all-zero row)
+ *     q[r, c]   = E4M3 code of the fp32 quotient w[r, c] / scale[r], rounded
+ *                 to nearest with ties to an even mantissa, saturating at 448.
+ * Expert weights quantize as rows = n*F (w1, w3) or n*d (w2), cols = d or F.
+ */
+moe_status_t moe_quantize_fp8(int64_t rows, int32_t cols, const void* w, uint8_t* q, float* scale,
+                              void* stream);
+
+/*
+ * FP8 variants of the expert projections and of the layer: desc->weight_dtype
+ * must be MOE_FP8_E4M3 (bf16 activations; d_model and d_ffn multiples of
+ * 1024), and the other expert entry points reject such a descriptor with
+ * MOE_ERR_INVALID_ARGUMENT.  Weights: w1, w3 [n, F, d] and w2 [n, d, F] codes;
+ * s1, s3 [n, F] and s2 [n, d] fp32 scales (16-byte aligned).  The products
+ * run on the exact E4M3 values in bf16 MFMAs with fp32 accumulation; each
+ * output's sum is multiplied by its row's scale before the SiLU gate (gate/up)
+ * or the store (down).  Always the weight-streaming kernels (tile_m 16):
+ * moe_permute's layout must be built with tile_m 16, and moe_workspace_size
+ * with tile_m 0 gives the layer's workspace.  Everything else is as for the
+ * bf16 calls of the same name.
+ */
+moe_status_t moe_expert_gate_up_fp8(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                    const int32_t* row_src, const int32_t* counts, const int32_t* offsets,
+                                    const uint8_t* w1, const float* s1, const uint8_t* w3, const float* s3,
+                                    void* h, void* stream);
+moe_status_t moe_expert_down_fp8(const moe_layer_desc_t* desc, int32_t T, const void* h, const int32_t* counts,
+                                 const int32_t* offsets, const uint8_t* w2, const float* s2, float* y_perm,
+                                 void* stream);
+moe_status_t moe_layer_forward_fp8(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                                   const uint8_t* w1, const float* s1, const uint8_t* w3, const float* s3,
+                                   const uint8_t* w2, const float* s2, const void* residual, void* y,
+                                   int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

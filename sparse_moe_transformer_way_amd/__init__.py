@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from ._lib import (  # noqa: F401
-    LIB_PATH, MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
+    LIB_PATH, MOE_BF16, MOE_FP8_E4M3, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE_TOO_SMALL, MOE_F32, MOE_OK, LayerDesc, MoeError, SIGNATURES, lib,
 )
 
@@ -24,18 +24,28 @@ __all__ = [
     "make_desc", "moe_version", "moe_default_tile_m", "moe_max_permuted_rows", "moe_workspace_size",
     "moe_router_topk", "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_swiglu",
     "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_block_workspace_size",
-    "moe_block_forward", "LayerDesc", "MoeError",
+    "moe_block_forward", "moe_quantize_fp8", "moe_expert_gate_up_fp8", "moe_expert_down_fp8",
+    "moe_layer_forward_fp8", "LayerDesc", "MoeError",
 ]
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
 
 def make_desc(d_model: int, d_ffn: int, n_experts: int = 8, top_k: int = 2,
-              dtype: torch.dtype = torch.bfloat16) -> LayerDesc:
+              dtype: torch.dtype = torch.bfloat16,
+              weight_dtype: Optional[torch.dtype] = None) -> LayerDesc:
+    """Layer descriptor.  weight_dtype defaults to dtype; torch.float8_e4m3fn
+    selects FP8 expert weights (bf16 activations, the *_fp8 calls)."""
     if dtype not in _DT:
         raise TypeError(f"unsupported dtype {dtype}")
     code = _DT[dtype]
-    return LayerDesc(d_model, d_ffn, n_experts, top_k, code, code)
+    if weight_dtype is None or weight_dtype == dtype:
+        wcode = code
+    elif weight_dtype == torch.float8_e4m3fn:
+        wcode = MOE_FP8_E4M3
+    else:
+        raise TypeError(f"unsupported weight dtype {weight_dtype}")
+    return LayerDesc(d_model, d_ffn, n_experts, top_k, code, wcode)
 
 
 def _act_dtype(desc: LayerDesc) -> torch.dtype:
@@ -238,3 +248,75 @@ def moe_block_forward(desc, h, w_gate, w1, w3, w2, eps: float = 1e-5, h_out=None
         _ptr(topk_idx_out, torch.int32, "topk_idx_out"), _ptr(counts_out, torch.int32, "counts_out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
     return h_out, topk_idx_out, counts_out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) expert weights: uint8 code tensors plus fp32 per-row scales
+# ---------------------------------------------------------------------------
+
+def moe_quantize_fp8(w, q=None, scale=None, stream=None):
+    """Per-row E4M3 quantization of a bf16 tensor [..., cols].
+    Returns (q uint8 of w's shape, scale fp32 [...])."""
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _check("moe_quantize_fp8", lib.moe_quantize_fp8(
+        rows, cols, _ptr(w, torch.bfloat16, "w"), _ptr(q, torch.uint8, "q"),
+        _ptr(scale, torch.float32, "scale"), _stream(stream)))
+    return q, scale
+
+
+def moe_expert_gate_up_fp8(desc, T, x, row_src, counts, offsets, w1, s1, w3, s3, h=None, stream=None):
+    """h = SiLU(s1 * (q1 . x)) * (s3 * (q3 . x)) over the grouped rows (tile_m 16).
+    Returns h [P_max, F] bf16."""
+    if h is None:
+        h = torch.empty((row_src.shape[0], desc.d_ffn), dtype=torch.bfloat16, device=x.device)
+    _check("moe_expert_gate_up_fp8", lib.moe_expert_gate_up_fp8(
+        desc, T, _ptr(x, torch.bfloat16, "x"), _ptr(row_src, torch.int32, "row_src"),
+        _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(w1, torch.uint8, "w1"), _ptr(s1, torch.float32, "s1"), _ptr(w3, torch.uint8, "w3"),
+        _ptr(s3, torch.float32, "s3"), _ptr(h, torch.bfloat16, "h"), _stream(stream)))
+    return h
+
+
+def moe_expert_down_fp8(desc, T, h, counts, offsets, w2, s2, y_perm=None, stream=None):
+    """y_perm = s2 * (q2 . h) over the grouped rows (tile_m 16).  Returns y_perm [P_max, d] fp32."""
+    if y_perm is None:
+        y_perm = torch.empty((h.shape[0], desc.d_model), dtype=torch.float32, device=h.device)
+    _check("moe_expert_down_fp8", lib.moe_expert_down_fp8(
+        desc, T, _ptr(h, torch.bfloat16, "h"), _ptr(counts, torch.int32, "counts"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(w2, torch.uint8, "w2"), _ptr(s2, torch.float32, "s2"),
+        _ptr(y_perm, torch.float32, "y_perm"), _stream(stream)))
+    return y_perm
+
+
+def moe_layer_forward_fp8(desc, x, w_gate, w1, s1, w3, s3, w2, s2, residual=None, y=None,
+                          topk_idx_out=None, topk_gate_out=None, counts_out=None, workspace=None,
+                          stream=None):
+    """The whole layer with FP8 expert weights.  Returns (y, topk_idx, topk_gate, counts)."""
+    T = x.shape[0]
+    dev = x.device
+    n, K = desc.n_experts, desc.top_k
+    bf = torch.bfloat16
+    if y is None:
+        y = torch.empty((T, desc.d_model), dtype=bf, device=dev)
+    if topk_idx_out is None:
+        topk_idx_out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_gate_out is None:
+        topk_gate_out = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if counts_out is None:
+        counts_out = torch.empty(n, dtype=torch.int32, device=dev)
+    need = lib.moe_workspace_size(desc, T, 0)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("moe_layer_forward_fp8", lib.moe_layer_forward_fp8(
+        desc, T, _ptr(x, bf, "x"), _ptr(w_gate, torch.float32, "w_gate"), _ptr(w1, torch.uint8, "w1"),
+        _ptr(s1, torch.float32, "s1"), _ptr(w3, torch.uint8, "w3"), _ptr(s3, torch.float32, "s3"),
+        _ptr(w2, torch.uint8, "w2"), _ptr(s2, torch.float32, "s2"), _ptr(residual, bf, "residual"),
+        _ptr(y, bf, "y"), _ptr(topk_idx_out, torch.int32, "topk_idx_out"),
+        _ptr(topk_gate_out, torch.float32, "topk_gate_out"), _ptr(counts_out, torch.int32, "counts_out"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return y, topk_idx_out, topk_gate_out, counts_out

@@ -19,6 +19,7 @@ MOE_ERR_HIP = 4
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_FP8_E4M3 = 2
 
 
 class LayerDesc(ctypes.Structure):
@@ -56,6 +57,11 @@ SIGNATURES = {
     "moe_block_workspace_size": (ctypes.c_size_t, [_desc, _i32]),
     "moe_block_forward": (_i32, [_desc, _i32, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p,
                                  ctypes.c_size_t, _p]),
+    "moe_quantize_fp8": (_i32, [ctypes.c_int64, _i32, _p, _p, _p, _p]),
+    "moe_expert_gate_up_fp8": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_expert_down_fp8": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_layer_forward_fp8": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, ctypes.c_size_t, _p]),
 }
 
 

@@ -22,9 +22,16 @@ moe_status_t check_desc(const moe_layer_desc_t* d) {
         return MOE_ERR_INVALID_ARGUMENT;
     if (d->top_k > d->n_experts) return MOE_ERR_INVALID_ARGUMENT;
     if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-    if (d->weight_dtype != MOE_F32 && d->weight_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (d->weight_dtype != MOE_F32 && d->weight_dtype != MOE_BF16 && d->weight_dtype != MOE_FP8_E4M3)
+        return MOE_ERR_INVALID_ARGUMENT;
     if (d->d_model % 8 != 0 || d->d_ffn % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
-    if (d->act_dtype != d->weight_dtype) return MOE_ERR_UNSUPPORTED;
+    if (d->weight_dtype == MOE_FP8_E4M3) {
+        // FP8 weights: bf16 activations, weight-streaming kernels (128-k stages per wave)
+        if (d->act_dtype != MOE_BF16 || d->d_model % 1024 != 0 || d->d_ffn % 1024 != 0)
+            return MOE_ERR_UNSUPPORTED;
+    } else if (d->act_dtype != d->weight_dtype) {
+        return MOE_ERR_UNSUPPORTED;
+    }
     if (d->n_experts > moe::kMaxExperts || d->top_k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
     if (d->act_dtype == MOE_BF16 && (d->d_model % 512 != 0 || d->d_ffn % 512 != 0))
         return MOE_ERR_UNSUPPORTED;
@@ -43,15 +50,18 @@ moe::Shape shape_of(const moe_layer_desc_t* d, int32_t T) {
     return moe::Shape{T, d->d_model, d->d_ffn, d->n_experts, d->top_k, d->act_dtype == MOE_BF16};
 }
 
+bool is_fp8(const moe_layer_desc_t* d) { return d->weight_dtype == MOE_FP8_E4M3; }
+
 int default_tile(const moe_layer_desc_t* d, int32_t T) {
-    if (d->act_dtype != MOE_BF16) return 16;
+    if (d->act_dtype != MOE_BF16 || is_fp8(d)) return 16;
     return (T <= 64 || !moe::tiled_fits(shape_of(d, T))) ? 16 : 256;
 }
 
 moe_status_t check_tile(const moe_layer_desc_t* d, int32_t T, int32_t tile_m) {
     if (tile_m == 16) return MOE_OK;
     if (tile_m == 256)
-        return (d->act_dtype == MOE_BF16 && moe::tiled_fits(shape_of(d, T))) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+        return (d->act_dtype == MOE_BF16 && !is_fp8(d) && moe::tiled_fits(shape_of(d, T))) ? MOE_OK
+                                                                                           : MOE_ERR_UNSUPPORTED;
     return MOE_ERR_INVALID_ARGUMENT;
 }
 
@@ -103,6 +113,69 @@ LayerWs carve_layer(const moe_layer_desc_t* d, int32_t T, int32_t tile_m, char* 
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The layer for either weight format (scales non-null = FP8).
+struct ExpertWeights {
+    const void* w1;
+    const void* w3;
+    const void* w2;
+    const float* s1;
+    const float* s3;
+    const float* s2;
+};
+
+moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                           const ExpertWeights& ew, const void* residual, void* y, int32_t* topk_idx_out,
+                           float* topk_gate_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    moe_status_t s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    const bool fp8 = is_fp8(desc);
+    if (x == nullptr || w_gate == nullptr || ew.w1 == nullptr || ew.w3 == nullptr || ew.w2 == nullptr ||
+        y == nullptr || workspace == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (fp8 && (ew.s1 == nullptr || ew.s3 == nullptr || ew.s2 == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (x == y) return MOE_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(ew.w1) || !aligned16(ew.w3) || !aligned16(ew.w2) ||
+        !aligned16(y) || (residual != nullptr && !aligned16(residual)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (fp8 && (!aligned16(ew.s1) || !aligned16(ew.s3) || !aligned16(ew.s2))) return MOE_ERR_INVALID_ARGUMENT;
+    const int tile_m = default_tile(desc, T);
+    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
+    if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    const moe::Shape sh = shape_of(desc, T);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
+    float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
+    int32_t* counts = counts_out != nullptr ? counts_out : w.counts;
+    if (moe::launch_router_topk(sh, x, w_gate, idx, gate, nullptr, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    int parts = 1;
+    if (fp8) {
+        const auto* q1 = static_cast<const uint8_t*>(ew.w1);
+        const auto* q3 = static_cast<const uint8_t*>(ew.w3);
+        const auto* q2 = static_cast<const uint8_t*>(ew.w2);
+        if (moe::launch_gate_up_fp8(sh, x, w.row_src, counts, w.offsets, q1, ew.s1, q3, ew.s3, w.h, st) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+        if (moe::launch_down_fp8(sh, w.h, counts, w.offsets, q2, ew.s2, w.y_perm, st) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        if (moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, ew.w1, ew.w3, w.h, st) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (moe::launch_down(sh, tile_m, w.h, counts, w.offsets, ew.w2, w.y_perm, st, w.y_perm_hi, &parts) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+    }
+    if (moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st, parts == 2 ? w.y_perm_hi : nullptr) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -175,6 +248,7 @@ moe_status_t moe_expert_gate_up(const moe_layer_desc_t* desc, int32_t T, int32_t
                                 void* stream) {
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
     if ((s = check_T(T, desc)) != MOE_OK) return s;
     if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
@@ -192,6 +266,7 @@ moe_status_t moe_expert_down(const moe_layer_desc_t* desc, int32_t T, int32_t ti
                              const void* w2, float* y_perm, void* stream) {
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
     if ((s = check_T(T, desc)) != MOE_OK) return s;
     if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
@@ -208,6 +283,7 @@ moe_status_t moe_grouped_swiglu(const moe_layer_desc_t* desc, int32_t T, int32_t
                                 const void* w2, void* h, float* y_perm, void* stream) {
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
     if ((s = check_T(T, desc)) != MOE_OK) return s;
     if ((s = check_tile(desc, T, tile_m)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
@@ -251,39 +327,9 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
                                void* workspace, size_t workspace_bytes, void* stream) {
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
-    if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if (T == 0) return MOE_OK;
-    if (x == nullptr || w_gate == nullptr || w1 == nullptr || w3 == nullptr || w2 == nullptr ||
-        y == nullptr || workspace == nullptr)
-        return MOE_ERR_INVALID_ARGUMENT;
-    if (x == y) return MOE_ERR_INVALID_ARGUMENT;
-    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
-    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) ||
-        !aligned16(y) || (residual != nullptr && !aligned16(residual)))
-        return MOE_ERR_INVALID_ARGUMENT;
-    const int tile_m = default_tile(desc, T);
-    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
-    if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
-
-    const moe::Shape sh = shape_of(desc, T);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
-    float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
-    int32_t* counts = counts_out != nullptr ? counts_out : w.counts;
-    hipError_t e;
-    if ((e = moe::launch_router_topk(sh, x, w_gate, idx, gate, nullptr, st)) != hipSuccess) return MOE_ERR_HIP;
-    if ((e = moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st)) != hipSuccess)
-        return MOE_ERR_HIP;
-    if ((e = moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, w1, w3, w.h, st)) != hipSuccess)
-        return MOE_ERR_HIP;
-    int parts = 1;
-    if ((e = moe::launch_down(sh, tile_m, w.h, counts, w.offsets, w2, w.y_perm, st, w.y_perm_hi, &parts)) !=
-        hipSuccess)
-        return MOE_ERR_HIP;
-    if ((e = moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st,
-                                 parts == 2 ? w.y_perm_hi : nullptr)) != hipSuccess)
-        return MOE_ERR_HIP;
-    return MOE_OK;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
+    return layer_forward(desc, T, x, w_gate, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr}, residual, y,
+                         topk_idx_out, topk_gate_out, counts_out, workspace, workspace_bytes, stream);
 }
 
 size_t moe_block_workspace_size(const moe_layer_desc_t* desc, int32_t T) {
@@ -299,6 +345,7 @@ moe_status_t moe_block_forward(const moe_layer_desc_t* desc, int32_t T, const vo
                                void* stream) {
     moe_status_t s = check_desc(desc);
     if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
     if (!(eps >= 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
     if (T == 0) return MOE_OK;
@@ -312,6 +359,61 @@ moe_status_t moe_block_forward(const moe_layer_desc_t* desc, int32_t T, const vo
     if (s != MOE_OK) return s;
     return moe_layer_forward(desc, T, ws, w_gate, w1, w3, w2, h, h_out, topk_idx_out, nullptr,
                              counts_out, ws + xn, workspace_bytes - xn, stream);
+}
+
+moe_status_t moe_quantize_fp8(int64_t rows, int32_t cols, const void* w, uint8_t* q, float* scale,
+                              void* stream) {
+    if (rows < 0 || rows > 0x7fffffffLL || cols <= 0 || cols % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return MOE_OK;
+    if (w == nullptr || q == nullptr || scale == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 7u) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_quantize_fp8(rows, cols, w, q, scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_gate_up_fp8(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                    const int32_t* row_src, const int32_t* counts, const int32_t* offsets,
+                                    const uint8_t* w1, const float* s1, const uint8_t* w3, const float* s3,
+                                    void* h, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (!is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (x == nullptr || row_src == nullptr || counts == nullptr || offsets == nullptr || w1 == nullptr ||
+        s1 == nullptr || w3 == nullptr || s3 == nullptr || h == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w3) || !aligned16(s1) || !aligned16(s3) || !aligned16(h))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_gate_up_fp8(shape_of(desc, T), x, row_src, counts, offsets, w1, s1, w3, s3, h,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_down_fp8(const moe_layer_desc_t* desc, int32_t T, const void* h, const int32_t* counts,
+                                 const int32_t* offsets, const uint8_t* w2, const float* s2, float* y_perm,
+                                 void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (!is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (h == nullptr || counts == nullptr || offsets == nullptr || w2 == nullptr || s2 == nullptr ||
+        y_perm == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(h) || !aligned16(w2) || !aligned16(s2) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_down_fp8(shape_of(desc, T), h, counts, offsets, w2, s2, y_perm,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_layer_forward_fp8(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                                   const uint8_t* w1, const float* s1, const uint8_t* w3, const float* s3,
+                                   const uint8_t* w2, const float* s2, const void* residual, void* y,
+                                   int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (!is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
+    return layer_forward(desc, T, x, w_gate, ExpertWeights{w1, w3, w2, s1, s3, s2}, residual, y, topk_idx_out,
+                         topk_gate_out, counts_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -14,11 +14,11 @@
 // runs.
 //
 // Three kernel families:
-//   * stream (tile_m 16, bf16): few rows per expert, the layer is bound by
-//     reading the expert weights once from HBM.  A block owns a slab of weight
-//     rows of one expert; its 4 waves split K, stream their weights straight
-//     into MFMA registers (no LDS staging: each weight is used by at most a few
-//     row blocks) and reduce through LDS.  Experts with no rows are skipped.
+//   * stream (tile_m 16, bf16 or FP8 weights): few rows per expert, the layer
+//     is bound by reading the expert weights once from HBM.  A block owns a
+//     slab of weight rows of one expert; its 4 waves split K, stream their
+//     weights through per-wave LDS slices into MFMA registers and reduce
+//     through LDS.  Experts with no rows are skipped.
 //   * tiled (tile_m 256, bf16): many rows per expert, MFMA-bound; in
 //     tiled_gemm.hip.
 //   * fp32 (tile_m 16): plain LDS-tiled FMA kernel for fp32 layers.
@@ -105,45 +105,85 @@ __device__ __forceinline__ void stream_copy(const StreamCtx& c, uint4* __restric
 
 typedef const __attribute__((address_space(1))) u32x4_t* gvec_t;
 
+// 16 E4M3 weights (k = 0..15 of a chunk, byte i = k i) to two bf16x8 MFMA
+// operands, k 0-7 and k 8-15.  E4M3 values are exact in bf16; the conversion
+// scale is 1.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& q, bf16x8_t& lo, bf16x8_t& hi) {
+    u32x4_t a, b;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        a[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[w], 1.0f, false));
+        a[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[w], 1.0f, true));
+        b[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[w + 2], 1.0f, false));
+        b[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[w + 2], 1.0f, true));
+    }
+    lo = as_bf16x8(a);
+    hi = as_bf16x8(b);
+}
+
 // One stage: token fragments from global memory, weight fragments from `cur`,
 // then (COPY) the next stage's copy into `nxt`, then the MFMAs.  Every lane
 // loads a real row (arow) and masks it (amask: all ones, or zero for a row
 // past the segment), so the loads stay plain global loads without branches.
-template <int NTP, bool COPY>
+//
+// bf16 weights: a stage is 64 k; step t (32 k) reads chunk 4t + g of the row
+// (k = 32t + 8g .. +8) and the token row at the same k.
+// FP8 weights: a stage is 128 k (still 128 bytes per row); step u (64 k)
+// reads chunk 4u + g, i.e. 16 weights k = 64u + 16g .. +16, which feed two
+// MFMAs (k 0-7 and 8-15 of the chunk); the token row is read at the same k.
+template <int NTP, bool COPY, bool FP8>
 __device__ __forceinline__ void stream_stage(const StreamCtx& c, const uint4* __restrict__ cur,
                                              uint4* __restrict__ nxt, int s,
                                              const bf16_t* const (&arow)[kStreamMaxTB],
                                              const uint32_t (&amask)[kStreamMaxTB],
                                              f32x4_t (&acc)[kStreamMaxTB][kStreamRB]) {
-    u32x4_t tv[NTP][2];
+    constexpr int kTV = FP8 ? 4 : 2;  // 8-element token fragments per stage
+    u32x4_t tv[NTP][kTV];
 #pragma unroll
     for (int tb = 0; tb < NTP; ++tb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tv[tb][t] = *(gvec_t)(arow[tb] + 64 * s + 32 * t);
+        for (int t = 0; t < kTV; ++t)
+            tv[tb][t] = FP8 ? *(gvec_t)(arow[tb] + 128 * s + 64 * (t >> 1) + 8 * (t & 1))
+                            : *(gvec_t)(arow[tb] + 64 * s + 32 * t);
 #pragma unroll
     for (int tb = 0; tb < NTP; ++tb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tv[tb][t] &= amask[tb];
+        for (int t = 0; t < kTV; ++t) tv[tb][t] &= amask[tb];
     u32x4_t wv[2][kStreamRB];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int b = 0; b < kStreamRB; ++b) wv[t][b] = __builtin_bit_cast(u32x4_t, cur[c.rd[t] + b * 128]);
     if (COPY) stream_copy(c, nxt, s + 1);
+    if constexpr (FP8) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int tb = 0; tb < NTP; ++tb)
+            for (int b = 0; b < kStreamRB; ++b) {
+                bf16x8_t lo, hi;
+                fp8x16_to_bf16(wv[u][b], lo, hi);
+#pragma unroll
+                for (int tb = 0; tb < NTP; ++tb) {
+                    acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, as_bf16x8(tv[tb][2 * u]), acc[tb][b], 0, 0, 0);
+                    acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, as_bf16x8(tv[tb][2 * u + 1]), acc[tb][b], 0, 0, 0);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int tb = 0; tb < NTP; ++tb)
 #pragma unroll
                 for (int b = 0; b < kStreamRB; ++b)
                     acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[t][b]), as_bf16x8(tv[tb][t]),
                                                                          acc[tb][b], 0, 0, 0);
+    }
     // keep the next stage's reads (which wait for its copy) after these MFMAs
     __builtin_amdgcn_sched_barrier(0);
 }
 
 // The K loop of one pass over NTP token blocks: ns stages (ns even, >= 2).
-template <int NTP>
+template <int NTP, bool FP8>
 __device__ __forceinline__ void stream_k_loop(const StreamCtx& c, uint4* sb0, uint4* sb1, int ns,
                                               const bf16_t* const (&arow)[kStreamMaxTB],
                                               const uint32_t (&amask)[kStreamMaxTB],
@@ -151,18 +191,21 @@ __device__ __forceinline__ void stream_k_loop(const StreamCtx& c, uint4* sb0, ui
     stream_copy(c, sb0, 0);
     int s = 0;
     for (; s + 2 < ns; s += 2) {
-        stream_stage<NTP, true>(c, sb0, sb1, s, arow, amask, acc);
-        stream_stage<NTP, true>(c, sb1, sb0, s + 1, arow, amask, acc);
+        stream_stage<NTP, true, FP8>(c, sb0, sb1, s, arow, amask, acc);
+        stream_stage<NTP, true, FP8>(c, sb1, sb0, s + 1, arow, amask, acc);
     }
-    stream_stage<NTP, true>(c, sb0, sb1, s, arow, amask, acc);
-    stream_stage<NTP, false>(c, sb1, sb0, s + 1, arow, amask, acc);
+    stream_stage<NTP, true, FP8>(c, sb0, sb1, s, arow, amask, acc);
+    stream_stage<NTP, false, FP8>(c, sb1, sb0, s + 1, arow, amask, acc);
 }
 
-template <bool DUAL>
+// FP8: wa/wb hold E4M3 codes and sa/sb one fp32 scale per weight row, applied
+// to the K sums before the epilogue; otherwise bf16 weights and no scales.
+template <bool DUAL, bool FP8>
 __global__ __launch_bounds__(256) void stream_kernel(
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
+    const void* __restrict__ wa, const void* __restrict__ wb, const float* __restrict__ sa,
+    const float* __restrict__ sb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P, int topk) {
     // Two stage buffers (each 4 wave slices of 8 KB); after the K loop they
     // hold the cross-wave reduction [wave][token block][weight block][lane].
@@ -183,7 +226,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int g = lane >> 4;
     const int kq = Kdim >> 2;
     const int kbeg = wave * kq;
-    const int ns = kq / 64;  // even (K is a multiple of 512)
+    constexpr int kEsz = FP8 ? 1 : 2;  // bytes per weight
+    // stages of 128 bytes per row: even (K is a multiple of 512, of 1024 for FP8)
+    const int ns = kq * kEsz / 128;
 
     StreamCtx c;
     {
@@ -191,16 +236,17 @@ __global__ __launch_bounds__(256) void stream_kernel(
         // reads logical chunk (l%8) ^ f(row) (f depends on the row's low bits only)
         const int rl = lane >> 3;
         const int lch = (lane & 7) ^ stream_swz(rl);
-        c.wo = (static_cast<uint32_t>(rl) * Kdim + 8u * lch) * 2u;
-        c.wgrp = 8 * Kdim * 2;
+        c.wo = static_cast<uint32_t>(rl) * Kdim * kEsz + 16u * lch;
+        c.wgrp = 8 * Kdim * kEsz;
+        const char* wab = static_cast<const char*>(wa);
         if (DUAL) {
             const size_t f0 = static_cast<size_t>(e) * Nw + blockIdx.x * 32;
-            c.wres[0] = stream_rsrc(wa + f0 * Kdim + kbeg);
-            c.wres[1] = stream_rsrc(wb + f0 * Kdim + kbeg);
+            c.wres[0] = stream_rsrc(wab + (f0 * Kdim + kbeg) * kEsz);
+            c.wres[1] = stream_rsrc(static_cast<const char*>(wb) + (f0 * Kdim + kbeg) * kEsz);
         } else {
             const size_t j0 = static_cast<size_t>(e) * Nw + blockIdx.x * 64;
-            c.wres[0] = stream_rsrc(wa + j0 * Kdim + kbeg);
-            c.wres[1] = stream_rsrc(wa + (j0 + 32) * Kdim + kbeg);
+            c.wres[0] = stream_rsrc(wab + (j0 * Kdim + kbeg) * kEsz);
+            c.wres[1] = stream_rsrc(wab + ((j0 + 32) * Kdim + kbeg) * kEsz);
         }
         c.slice = wave * kStreamWaveVec;
 #pragma unroll
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                     row = p;
                 }
             }
-            arow[tb] = act + static_cast<size_t>(row) * ld_act + kbeg + 8 * g;
+            arow[tb] = act + static_cast<size_t>(row) * ld_act + kbeg + (FP8 ? 16 : 8) * g;
             amask[tb] = real ? 0xffffffffu : 0u;
         }
 
@@ -242,10 +288,10 @@ __global__ __launch_bounds__(256) void stream_kernel(
             for (int b = 0; b < kStreamRB; ++b) acc[tb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         switch (ntp) {
-            case 1: stream_k_loop<1>(c, sb0, sb1, ns, arow, amask, acc); break;
-            case 2: stream_k_loop<2>(c, sb0, sb1, ns, arow, amask, acc); break;
-            case 3: stream_k_loop<3>(c, sb0, sb1, ns, arow, amask, acc); break;
-            default: stream_k_loop<4>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 1: stream_k_loop<1, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 2: stream_k_loop<2, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 3: stream_k_loop<3, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
+            default: stream_k_loop<4, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
         }
 
         // Cross-wave K reduction in a fixed order through the stage buffers,
@@ -280,7 +326,12 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * Nw;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const f32x4_t a1 = sum[half], a3 = sum[half + 2];
+                    f32x4_t a1 = sum[half], a3 = sum[half + 2];
+                    if constexpr (FP8) {
+                        const size_t f = static_cast<size_t>(e) * Nw + f0 + half * 16 + 4 * g;
+                        a1 *= *reinterpret_cast<const f32x4_t*>(sa + f);
+                        a3 *= *reinterpret_cast<const f32x4_t*>(sb + f);
+                    }
                     uint2 o;
                     o.x = pack_bf16x2(silu_f32(a1[0]) * a3[0], silu_f32(a1[1]) * a3[1]);
                     o.y = pack_bf16x2(silu_f32(a1[2]) * a3[2], silu_f32(a1[3]) * a3[3]);
@@ -290,8 +341,11 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 const int j0 = blockIdx.x * 64;
                 float* yrow = static_cast<float*>(out) + static_cast<size_t>(p) * Nw;
 #pragma unroll
-                for (int b = 0; b < kStreamRB; ++b)
+                for (int b = 0; b < kStreamRB; ++b) {
+                    if constexpr (FP8)
+                        sum[b] *= *reinterpret_cast<const f32x4_t*>(sa + static_cast<size_t>(e) * Nw + j0 + b * 16 + 4 * g);
                     *reinterpret_cast<f32x4_t*>(yrow + j0 + b * 16 + 4 * g) = sum[b];
+                }
             }
         }
         __syncthreads();
@@ -407,10 +461,9 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
                                                pmax_rows(s, 16), s.n, s.K);
     } else if (tile_m == 16) {
         dim3 grid(s.F / 32, s.n);
-        stream_kernel<true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts,
-                                                  offsets, static_cast<const bf16_t*>(w1),
-                                                  static_cast<const bf16_t*>(w3), h, s.d, s.F, s.d,
-                                                  s.T * s.K, pmax_rows(s, 16), s.K);
+        stream_kernel<true, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts,
+                                                         offsets, w1, w3, nullptr, nullptr, h, s.d, s.F, s.d,
+                                                         s.T * s.K, pmax_rows(s, 16), s.K);
     } else {
         return launch_tiled(s, true, x, row_src, counts, offsets, w1, w3, h, st);
     }
@@ -429,10 +482,10 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
                                                 pmax_rows(s, 16), s.n, s.K);
     } else if (tile_m == 16) {
         dim3 grid(s.d / 64, s.n);
-        stream_kernel<false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts,
-                                                   offsets, static_cast<const bf16_t*>(w2), nullptr,
-                                                   y_perm, s.F, s.d, s.F, s.T * s.K,
-                                                   pmax_rows(s, 16), s.K);
+        stream_kernel<false, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts,
+                                                          offsets, w2, nullptr, nullptr, nullptr,
+                                                          y_perm, s.F, s.d, s.F, s.T * s.K,
+                                                          pmax_rows(s, 16), s.K);
     } else {
         int ks = 1;
         if (y_perm_hi != nullptr) {
@@ -444,6 +497,25 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
         if (n_parts != nullptr) *n_parts = ks;
         return launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_fp8(const Shape& s, const void* x, const int32_t* row_src, const int32_t* counts,
+                              const int32_t* offsets, const uint8_t* w1, const float* s1, const uint8_t* w3,
+                              const float* s3, void* h, hipStream_t st) {
+    dim3 grid(s.F / 32, s.n);
+    stream_kernel<true, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts, offsets, w1,
+                                                    w3, s1, s3, h, s.d, s.F, s.d, s.T * s.K, pmax_rows(s, 16),
+                                                    s.K);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_fp8(const Shape& s, const void* h, const int32_t* counts, const int32_t* offsets,
+                           const uint8_t* w2, const float* s2, float* y_perm, hipStream_t st) {
+    dim3 grid(s.d / 64, s.n);
+    stream_kernel<false, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts, offsets, w2,
+                                                     nullptr, s2, nullptr, y_perm, s.F, s.d, s.F, s.T * s.K,
+                                                     pmax_rows(s, 16), s.K);
     return hipGetLastError();
 }
 

@@ -87,6 +87,17 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
                        const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
                        float* y_perm_hi = nullptr, int* n_parts = nullptr);
 
+// FP8 (E4M3) expert weights, weight-streaming kernels (tile_m 16, bf16
+// activations): w1/w3 [n, F, d] and w2 [n, d, F] codes with one fp32 scale per
+// row (s1, s3 [n, F], s2 [n, d]).  d and F must be multiples of 1024.
+hipError_t launch_gate_up_fp8(const Shape& s, const void* x, const int32_t* row_src, const int32_t* counts,
+                              const int32_t* offsets, const uint8_t* w1, const float* s1, const uint8_t* w3,
+                              const float* s3, void* h, hipStream_t st);
+hipError_t launch_down_fp8(const Shape& s, const void* h, const int32_t* counts, const int32_t* offsets,
+                           const uint8_t* w2, const float* s2, float* y_perm, hipStream_t st);
+// Per-row E4M3 quantization of a bf16 [rows, cols] matrix (cols % 8 == 0).
+hipError_t launch_quantize_fp8(int64_t rows, int cols, const void* w, uint8_t* q, float* scale, hipStream_t st);
+
 // Whether the tiled kernels can address this shape's token rows (gate/up
 // reaches the rows of x through 32-bit byte offsets: T * d_model * 2 bytes
 // must stay below 4 GiB).

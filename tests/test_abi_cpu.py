@@ -139,3 +139,44 @@ def test_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         moe.moe_router_topk(d, torch.zeros(2, 4096, dtype=torch.bfloat16),
                             torch.zeros(4096, 8))
+
+
+def test_fp8_descriptor_rules():
+    """FP8 expert weights: bf16 activations, d and F multiples of 1024, tile 16
+    only; the bf16 expert calls and the FP8 calls each reject the other's
+    descriptor before any launch."""
+    f8 = D(weight_dtype=2)
+    assert moe.moe_default_tile_m(f8, 1000) == 16
+    assert moe.moe_workspace_size(f8, 100, 256) == 0
+    assert moe.moe_workspace_size(f8, 100, 0) == moe.moe_workspace_size(D(), 100, 16) > 0
+    assert moe.moe_workspace_size(D(weight_dtype=2, d_model=1536), 10, 0) == 0
+    assert moe.moe_workspace_size(D(weight_dtype=2, act_dtype=0), 10, 0) == 0
+    assert moe.moe_workspace_size(D(weight_dtype=3), 10, 0) == 0
+    lib = _lib.lib
+    p8, pb = ctypes.byref(f8), ctypes.byref(D())
+    assert lib.moe_expert_gate_up(p8, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_expert_down(p8, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_grouped_swiglu(p8, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_layer_forward(p8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096, None, None, None,
+                                 FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_gate_up_fp8(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_expert_down_fp8(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_layer_forward_fp8(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096,
+                                     None, None, None, FAKE, 1 << 30, None) == 1
+    assert lib.moe_expert_down_fp8(p8, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1      # no scales
+    assert lib.moe_expert_gate_up_fp8(p8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE,
+                                      None) == 1                                              # misaligned s1
+    assert lib.moe_layer_forward_fp8(p8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE + 4096,
+                                     None, None, None, FAKE, 1 << 30, None) == 1              # no s3
+    assert lib.moe_expert_gate_up_fp8(p8, 0, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_quantize_fp8_argument_checks():
+    lib = _lib.lib
+    assert lib.moe_quantize_fp8(10, 12, FAKE, FAKE, FAKE, None) == 1        # cols % 8
+    assert lib.moe_quantize_fp8(-1, 16, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_quantize_fp8(1 << 31, 16, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_quantize_fp8(10, 16, FAKE + 4, FAKE, FAKE, None) == 1    # w alignment
+    assert lib.moe_quantize_fp8(10, 16, FAKE, FAKE + 4, FAKE, None) == 1    # q alignment
+    assert lib.moe_quantize_fp8(10, 16, FAKE, FAKE, None, None) == 1
+    assert lib.moe_quantize_fp8(0, 16, None, None, None, None) == 0
