@@ -488,3 +488,85 @@ def test_fp8_error_against_plain_layer():
     rms = np.sqrt(((got["y"] - ref["y"]) ** 2).mean(axis=1) / (ref["y"] ** 2).mean(axis=1))
     assert err.max() < 0.10
     assert 0.03 < np.median(rms) < 0.06
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+
+def _bwd_case(seed, T=12, d=16, F=24, n=8, K=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((d, n)) * 0.5
+    w1 = rng.standard_normal((n, F, d)) / np.sqrt(d)
+    w3 = rng.standard_normal((n, F, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((n, d, F)) / np.sqrt(F)
+    dy = rng.standard_normal((T, d))
+    return x, wg, w1, w3, w2, dy
+
+
+@pytest.mark.parametrize("n,K", [(8, 2), (8, 1), (6, 3), (4, 4)])
+def test_backward_vs_torch_autograd(n, K):
+    """Every gradient against torch autograd on a float64 dense formulation
+    (the TopK selection is taken from the forward oracle and held fixed, as
+    it is piecewise constant)."""
+    x, wg, w1, w3, w2, dy = _bwd_case(20 + n + K, n=n, K=K)
+    g = oracle.moe_layer_backward(x, wg, w1, w3, w2, dy, K=K)
+    tx, twg, tw1, tw3, tw2 = (torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                              for a in (x, wg, w1, w3, w2))
+    logits = tx @ twg
+    mask = torch.zeros_like(logits, dtype=torch.bool)
+    mask[torch.arange(x.shape[0])[:, None], torch.from_numpy(g["idx"].astype(np.int64))] = True
+    G = torch.softmax(logits.masked_fill(~mask, float("-inf")), dim=1)
+    y = 0
+    for i in range(n):
+        a1 = tx @ tw1[i].T
+        hh = torch.nn.functional.silu(a1) * (tx @ tw3[i].T)
+        y = y + G[:, i:i + 1] * (hh @ tw2[i].T)
+    (y * torch.from_numpy(dy)).sum().backward()
+    for name, t in (("dx", tx), ("dwg", twg), ("dw1", tw1), ("dw3", tw3), ("dw2", tw2)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_backward_vs_finite_differences():
+    """Central differences of the float64 forward at random coordinates of
+    every input (routing margins checked so that no step changes the
+    selection)."""
+    x, wg, w1, w3, w2, dy = _bwd_case(31, T=6, d=8, F=10, n=6, K=2)
+    g = oracle.moe_layer_backward(x, wg, w1, w3, w2, dy, K=2)
+    s = -np.sort(-(x @ wg), axis=1)
+    assert (s[:, 1] - s[:, 2]).min() > 1e-3
+    rng = np.random.default_rng(5)
+    args = [x, wg, w1, w3, w2]
+    names = ["dx", "dwg", "dw1", "dw3", "dw2"]
+    eps = 1e-6
+    for ai, name in enumerate(names):
+        for _ in range(6):
+            pos = tuple(rng.integers(0, m) for m in args[ai].shape)
+            lo = [a.copy() for a in args]
+            hi = [a.copy() for a in args]
+            lo[ai][pos] -= eps
+            hi[ai][pos] += eps
+            f_hi = (oracle.forward64(*hi, K=2)["y"] * dy).sum()
+            f_lo = (oracle.forward64(*lo, K=2)["y"] * dy).sum()
+            fd = (f_hi - f_lo) / (2 * eps)
+            assert abs(fd - g[name][pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, g[name][pos])
+
+
+def test_backward_top1_closed_form():
+    """K = 1: the gate is exactly 1, so the router gets no gradient and the
+    layer's gradients are those of the selected expert alone."""
+    x, wg, w1, w3, w2, dy = _bwd_case(41, n=5, K=1)
+    g = oracle.moe_layer_backward(x, wg, w1, w3, w2, dy, K=1)
+    assert (g["dwg"] == 0).all()
+    for t in range(x.shape[0]):
+        e = g["idx"][t, 0]
+        a1, a3 = w1[e] @ x[t], w3[e] @ x[t]
+        s = 1 / (1 + np.exp(-a1))
+        dh = w2[e].T @ dy[t]
+        dx = w1[e].T @ (dh * a3 * s * (1 + a1 * (1 - s))) + w3[e].T @ (dh * a1 * s)
+        np.testing.assert_allclose(g["dx"][t], dx, rtol=1e-12, atol=1e-12)
+    for e in range(5):
+        sel = g["idx"][:, 0] == e
+        h = (x[sel] @ w1[e].T) * (1 / (1 + np.exp(-(x[sel] @ w1[e].T)))) * (x[sel] @ w3[e].T)
+        np.testing.assert_allclose(g["dw2"][e], dy[sel].T @ h, rtol=1e-12, atol=1e-12)
