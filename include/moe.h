@@ -254,6 +254,34 @@ moe_status_t moe_layer_forward_fp8(const moe_layer_desc_t* desc, int32_t T, cons
                                    int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass of the layer (bf16 activations and weights).  For the upstream
+ * gradient dy of y = sum_i G(x)_i E_i(x) it writes the gradients of
+ * sum(dy * y) with respect to every input, by the chain rule through the
+ * gating equation, the TopK selection (held fixed: masked logits get no
+ * gradient), the softmax over the K survivors and the SwiGLU experts
+ * (paper-graph-ui page, section 3.4: gating, TopK, output and SwiGLU
+ * equations):
+ *   dx      [T, d]     bf16 out (must not alias x or dy)
+ *   dw_gate [d, n]     fp32 out
+ *   dw1, dw3 [n, F, d], dw2 [n, d, F]   fp32 out (overwritten, not accumulated)
+ * Nothing of the forward pass is needed: the routing and the gate/up
+ * pre-activations are recomputed from x.  Arithmetic: bf16 MFMA products with
+ * fp32 accumulation; the pre-activations stay fp32, their gradients and g*h
+ * are rounded once to bf16 (the operands of the next products); every
+ * reduction over tokens runs in fp32 in a fixed order (deterministic).
+ * T == 0 writes zero weight gradients.  Supported: bf16 layers whose per-row
+ * buffers stay below 2 GiB (T * K + 127 n rows of 2F fp32); else
+ * MOE_ERR_UNSUPPORTED.
+ * workspace: at least moe_backward_workspace_size(desc, T) bytes, 256-byte
+ * aligned (0 = unsupported descriptor).
+ */
+size_t moe_backward_workspace_size(const moe_layer_desc_t* desc, int32_t T);
+moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                                const void* w1, const void* w3, const void* w2, const void* dy, void* dx,
+                                float* dw_gate, float* dw1, float* dw3, float* dw2, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

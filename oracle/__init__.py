@@ -11,4 +11,4 @@ from .moe_oracle import (  # noqa: F401
 from .fp8 import (  # noqa: F401
     e4m3_decode, e4m3_encode_rne, quantize_rows_fp8, dequantize_rows_fp8, moe_layer_fp8,
 )
-from .backward import forward64, moe_layer_backward  # noqa: F401
+from .backward import backward_expert_rows, backward_token_rows, forward64, moe_layer_backward  # noqa: F401

@@ -89,3 +89,63 @@ def moe_layer_backward(x, wg, w1, w3, w2, dy, K: int = 2) -> dict:
     dw3 = np.einsum("ntf,td->nfd", da3, x)
     dx = dx + np.einsum("ntf,nfd->td", da1, w1) + np.einsum("ntf,nfd->td", da3, w3)
     return dict(dx=dx, dwg=dwg, dw1=dw1, dw3=dw3, dw2=dw2, idx=fw["idx"], G=G)
+
+
+def _route64(x, wg, K):
+    logits = np.asarray(x, F64) @ np.asarray(wg, F64)
+    idx = topk_indices(logits, K)
+    rows = np.arange(logits.shape[0])[:, None]
+    masked = np.full_like(logits, -np.inf)
+    masked[rows, idx] = logits[rows, idx]
+    e = np.exp(masked - masked.max(axis=1, keepdims=True))
+    return idx, e / e.sum(axis=1, keepdims=True)
+
+
+def backward_token_rows(x, wg, w1, w3, w2, dy, tokens, K: int = 2) -> dict:
+    """dx and dl (router logit gradients) of the given tokens only, each token
+    from its K selected experts (the experts with G = 0 contribute nothing),
+    float64.  The same formulas as moe_layer_backward, for large layers."""
+    tokens = np.asarray(tokens)
+    xs = np.asarray(x, F64)[tokens]
+    dys = np.asarray(dy, F64)[tokens]
+    wg = np.asarray(wg, F64)
+    idx, G = _route64(xs, wg, K)
+    n = wg.shape[1]
+    dG = np.zeros_like(G)
+    cache = {}
+    for e in np.unique(idx):
+        S = np.nonzero((idx == e).any(axis=1))[0]
+        w1e, w3e, w2e = (np.asarray(w[e], F64) for w in (w1, w3, w2))
+        a1 = xs[S] @ w1e.T
+        a3 = xs[S] @ w3e.T
+        h = a1 * _sigmoid(a1) * a3
+        dG[S, e] = (dys[S] * (h @ w2e.T)).sum(axis=1)
+        cache[e] = (S, w1e, w3e, w2e, a1, a3)
+    dl = G * (dG - (G * dG).sum(axis=1, keepdims=True))
+    dx = dl @ wg.T
+    for e, (S, w1e, w3e, w2e, a1, a3) in cache.items():
+        dh = (G[S, e][:, None] * dys[S]) @ w2e
+        s = _sigmoid(a1)
+        dx[S] += (dh * a3 * s * (1.0 + a1 * (1.0 - s))) @ w1e + (dh * a1 * s) @ w3e
+    return dict(dx=dx, dl=dl, idx=idx, G=G, n=n)
+
+
+def backward_expert_rows(x, wg, w1, w3, w2, dy, e: int, f_rows, j_rows, K: int = 2) -> dict:
+    """Rows f_rows of dw1[e] and dw3[e] and rows j_rows of dw2[e], float64,
+    summed over every token routed to expert e."""
+    x64 = np.asarray(x, F64)
+    idx, G = _route64(x64, wg, K)
+    S = np.nonzero((idx == e).any(axis=1))[0]
+    xs, dys, gs = x64[S], np.asarray(dy, F64)[S], G[S, e]
+    w1e, w3e, w2e = (np.asarray(w[e], F64) for w in (w1, w3, w2))
+    a1 = xs @ w1e.T
+    a3 = xs @ w3e.T
+    h = a1 * _sigmoid(a1) * a3
+    dw2 = (gs[:, None] * dys[:, j_rows]).T @ h
+    f_rows = np.asarray(f_rows)
+    dh = gs[:, None] * (dys @ w2e[:, f_rows])
+    a1f, a3f = a1[:, f_rows], a3[:, f_rows]
+    s = _sigmoid(a1f)
+    dw1 = (dh * a3f * s * (1.0 + a1f * (1.0 - s))).T @ xs
+    dw3 = (dh * a1f * s).T @ xs
+    return dict(dw1=dw1, dw3=dw3, dw2=dw2, count=S.size)

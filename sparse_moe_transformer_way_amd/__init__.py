@@ -25,7 +25,7 @@ __all__ = [
     "moe_router_topk", "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_swiglu",
     "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_block_workspace_size",
     "moe_block_forward", "moe_quantize_fp8", "moe_expert_gate_up_fp8", "moe_expert_down_fp8",
-    "moe_layer_forward_fp8", "LayerDesc", "MoeError",
+    "moe_layer_forward_fp8", "moe_backward_workspace_size", "moe_layer_backward", "LayerDesc", "MoeError",
 ]
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
@@ -320,3 +320,40 @@ def moe_layer_forward_fp8(desc, x, w_gate, w1, s1, w3, s3, w2, s2, residual=None
         _ptr(topk_gate_out, torch.float32, "topk_gate_out"), _ptr(counts_out, torch.int32, "counts_out"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
     return y, topk_idx_out, topk_gate_out, counts_out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+
+def moe_backward_workspace_size(desc, T: int) -> int:
+    return lib.moe_backward_workspace_size(desc, T)
+
+
+def moe_layer_backward(desc, x, w_gate, w1, w3, w2, dy, dx=None, dw_gate=None, dw1=None, dw3=None, dw2=None,
+                       workspace=None, stream=None):
+    """Gradients of sum(dy * y) for the bf16 layer.
+    Returns (dx bf16 [T, d], dw_gate fp32 [d, n], dw1, dw3 fp32 [n, F, d], dw2 fp32 [n, d, F])."""
+    T = x.shape[0]
+    dev = x.device
+    n, d, F = desc.n_experts, desc.d_model, desc.d_ffn
+    bf, f32 = torch.bfloat16, torch.float32
+    if dx is None:
+        dx = torch.empty((T, d), dtype=bf, device=dev)
+    if dw_gate is None:
+        dw_gate = torch.empty((d, n), dtype=f32, device=dev)
+    if dw1 is None:
+        dw1 = torch.empty((n, F, d), dtype=f32, device=dev)
+    if dw3 is None:
+        dw3 = torch.empty((n, F, d), dtype=f32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((n, d, F), dtype=f32, device=dev)
+    need = lib.moe_backward_workspace_size(desc, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("moe_layer_backward", lib.moe_layer_backward(
+        desc, T, _ptr(x, bf, "x"), _ptr(w_gate, f32, "w_gate"), _ptr(w1, bf, "w1"), _ptr(w3, bf, "w3"),
+        _ptr(w2, bf, "w2"), _ptr(dy, bf, "dy"), _ptr(dx, bf, "dx"), _ptr(dw_gate, f32, "dw_gate"),
+        _ptr(dw1, f32, "dw1"), _ptr(dw3, f32, "dw3"), _ptr(dw2, f32, "dw2"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return dx, dw_gate, dw1, dw3, dw2

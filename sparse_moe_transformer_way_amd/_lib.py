@@ -62,6 +62,9 @@ SIGNATURES = {
     "moe_expert_down_fp8": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_layer_forward_fp8": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                      _p, ctypes.c_size_t, _p]),
+    "moe_backward_workspace_size": (ctypes.c_size_t, [_desc, _i32]),
+    "moe_layer_backward": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  ctypes.c_size_t, _p]),
 }
 
 

@@ -416,4 +416,41 @@ moe_status_t moe_layer_forward_fp8(const moe_layer_desc_t* desc, int32_t T, cons
                          topk_gate_out, counts_out, workspace, workspace_bytes, stream);
 }
 
+size_t moe_backward_workspace_size(const moe_layer_desc_t* desc, int32_t T) {
+    if (check_desc(desc) != MOE_OK || check_T(T, desc) != MOE_OK) return 0;
+    if (desc->act_dtype != MOE_BF16 || is_fp8(desc)) return 0;
+    const moe::Shape sh = shape_of(desc, T);
+    if (!moe::backward_fits(sh)) return 0;
+    return moe::backward_workspace_bytes(sh, nullptr, nullptr);
+}
+
+moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                                const void* w1, const void* w3, const void* w2, const void* dy, void* dx,
+                                float* dw_gate, float* dw1, float* dw3, float* dw2, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (desc->act_dtype != MOE_BF16 || is_fp8(desc)) return MOE_ERR_UNSUPPORTED;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    const moe::Shape sh = shape_of(desc, T);
+    if (!moe::backward_fits(sh)) return MOE_ERR_UNSUPPORTED;
+    if (dw_gate == nullptr || dw1 == nullptr || dw3 == nullptr || dw2 == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dw_gate) || !aligned16(dw1) || !aligned16(dw3) || !aligned16(dw2))
+        return MOE_ERR_INVALID_ARGUMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) return hip_status(moe::launch_zero_grads(sh, dw_gate, dw1, dw3, dw2, st));
+    if (x == nullptr || w_gate == nullptr || w1 == nullptr || w3 == nullptr || w2 == nullptr || dy == nullptr ||
+        dx == nullptr || workspace == nullptr)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (dx == x || dx == dy) return MOE_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) ||
+        !aligned16(dy) || !aligned16(dx))
+        return MOE_ERR_INVALID_ARGUMENT;
+    moe::BackwardWs w;
+    if (workspace_bytes < moe::backward_workspace_bytes(sh, &w, static_cast<char*>(workspace)))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(moe::launch_layer_backward(sh, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2, w, st));
+}
+
 }  // extern "C"

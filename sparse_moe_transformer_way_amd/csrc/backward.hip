@@ -1,0 +1,713 @@
+// Backward pass of the Mixtral sparse-MoE layer (bf16 activations and weights,
+// fp32 gradients of the weights).
+//
+// The layer is y = sum_i G(x)_i E_i(x), G(x) = Softmax(TopK(x . W_g)),
+// E_i(x) = w2_i . (SiLU(w1_i . x) * (w3_i . x)) (Mixtral of Experts,
+// paper-graph-ui page, section 3.4: gating, output and SwiGLU equations).  By
+// the chain rule, for a routed assignment (token t, slot s, expert e, gate g)
+// at permuted row p:
+//   G_p   = w2_e^T dy_t                  [F]   (unscaled down-projection gradient)
+//   dg_s  = G_p . h_p                          (= dy_t . E_e(x_t))
+//   dh_p  = g G_p,  da3 = dh SiLU(a1),  da1 = dh a3 SiLU'(a1)
+//   dx_t += w1_e^T da1 + w3_e^T da3
+//   dw2_e += g dy_t (x) h_p,  dw1_e += da1 (x) x_t,  dw3_e += da3 (x) x_t
+// and the router gradient is the softmax Jacobian on the K selected logits:
+//   dl_s = g_s (dg_s - sum_j g_j dg_j),  dW_g += x_t (x) dl,  dx_t += W_g dl.
+//
+// The pass recomputes the routing and the gate/up pre-activations a1, a3
+// (nothing of the forward pass is kept), then runs five grouped GEMMs through
+// one MFMA kernel, over the expert-grouped rows padded to 128:
+//   1. a = [a1 | a3] = xp . [w1; w3]^T       u = 2F features, v = rows, K = d (fp32)
+//   2. G = dyp . w2                           u = F, v = rows, K = d; epilogue
+//      forms h, dg partial sums, da = [da1 | da3] and hg = g h
+//   3. dxp = da . [w1; w3]                    u = d, v = rows, K = 2F
+//   4. dw2_e = hg^T dyp                       u = F, v = d, K = the expert's rows
+//   5. [dw1; dw3]_e = xp^T da                 u = d, v = 2F, K = the expert's rows
+// where xp, dyp are x and dy gathered into permuted rows (zero for padding).
+//
+// The GEMM computes C[u][v] = sum_k X[u][k] Y[v][k].  Each operand is stored
+// either k-contiguous ([rows][k]) or row-contiguous ([k][rows]); both are
+// copied into LDS unchanged by buffer loads with the LDS bit.  Row-contiguous
+// tiles feed the MFMAs through the transposing LDS read of gfx950
+// (ds_read_b64_tr_b16): in a 16-lane group, lane i addresses row k0 + i/4,
+// columns c0 + 4(i%4) .. +3 of a [k][c] tile, and lane j = 4a + b receives
+// element b of lanes a, a+4, a+8, a+12, i.e. column c0 + j at k0 .. k0+3 (the
+// lane layout was measured on MI355X).
+#include "moe_common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTU = 256;  // block tile along u (MFMA rows)
+constexpr int kTV = 128;  // block tile along v (MFMA columns); row padding of the layout
+constexpr int kBK = 32;   // k per stage
+constexpr int kXVec = kTU * kBK * 2 / 16;  // uint4 of an X stage (16 KB)
+constexpr int kYVec = kTV * kBK * 2 / 16;  // uint4 of a Y stage (8 KB)
+constexpr int kStageVec = kXVec + kYVec;
+
+typedef void __attribute__((address_space(3)))* lds_ptr_t;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t* lds_v4s_t;
+typedef __attribute__((address_space(3))) char* lds_char_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const void* base) {
+    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting of gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// Operand copies and fragment reads
+// ---------------------------------------------------------------------------
+//
+// k-contiguous tile, ROWS x 32 k, 64 bytes per row: 16-byte granule g of row r
+// sits at g ^ f(r), f(r) = ((r >> 2) ^ (r >> 3)) & 3, so the 16 rows of a
+// fragment-read phase hit 16 distinct 4-bank groups.  One copy instruction
+// fills 16 rows (lane l: row l/4, physical granule l%4).
+// Row-contiguous tile, 32 k x ROWS, 2*ROWS bytes per k-row: granule g of k-row
+// k sits at g ^ 4(k & 3), so the 4 k-rows of a transposing read land in 4
+// different bank groups.  One copy instruction fills 512/ROWS k-rows.
+
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 3; }
+
+// (a plain struct: the host pass of hipcc rejects a class template holding a
+// buffer resource once two kernels share a helper that passes it to a builtin)
+struct Operand {
+    __amdgpu_buffer_rsrc_t res[2];  // source halves (the second from stage `split` on)
+    uint32_t vo[2];                 // lane byte offset, by copy-instruction parity
+    uint32_t wfirst;                // bytes from the tile origin to this wave's first copy
+    uint32_t jstep;                 // bytes between this wave's copy instructions
+    uint32_t kstep;                 // bytes per stage
+    int split;                      // first stage read from res[1]
+    int rd[4];                      // lane byte offsets of the fragment reads (per 32-row block class)
+};
+
+// Copy set-up for an operand whose memory rows have `ld` elements.  The tile's
+// origin (row 0 / k 0) is the resource base.
+template <bool RC, int ROWS>
+__device__ __forceinline__ void operand_setup(Operand& o, int ld, int wave, int lane) {
+    constexpr int kInstr = ROWS / 64;  // copy instructions per thread per stage
+    if (!RC) {
+        // instruction j of wave w: rows w*ROWS/4 + 16j .. +15
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int row = wave * (ROWS / 4) + 16 * par + (lane >> 2);
+            const int glog = (lane & 3) ^ kc_swz(row);
+            o.vo[par] = static_cast<uint32_t>((lane >> 2) * ld + 8 * glog) * 2u;
+        }
+        o.wfirst = static_cast<uint32_t>(wave * (ROWS / 4)) * ld * 2u;
+        o.jstep = 16u * ld * 2u;
+        o.kstep = kBK * 2;
+    } else {
+        constexpr int kKR = 512 / ROWS;        // k-rows per copy instruction
+        constexpr int kGr = ROWS / 8;          // granules per k-row
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int k = (wave * kInstr + par) * kKR + lane / kGr;
+            const int glog = (lane % kGr) ^ (4 * (k & 3));
+            o.vo[par] = static_cast<uint32_t>((lane / kGr) * ld + 8 * glog) * 2u;
+        }
+        o.wfirst = static_cast<uint32_t>(wave * kInstr * kKR) * ld * 2u;
+        o.jstep = static_cast<uint32_t>(kKR) * ld * 2u;
+        o.kstep = static_cast<uint32_t>(kBK) * ld * 2u;
+    }
+}
+
+// Fragment-read offsets: `rb` = first row of the wave's part of the tile
+// (a multiple of 32); block b adds 32 rows.
+template <bool RC, int ROWS>
+__device__ __forceinline__ void operand_reads(Operand& o, int rb, int lane) {
+    const int fk = lane >> 5;
+    if (!RC) {
+        // 32x32x16 operand: lane (r = l%32, fk) takes k 8fk..8fk+7 of row r;
+        // class t = k16 step (0, 1) of the stage; blocks add 32 rows (f unchanged)
+        const int row = rb + (lane & 31);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) o.rd[t] = row * 64 + (((2 * t + fk) ^ kc_swz(row)) << 4);
+    } else {
+        // transposing reads: lane i of a 16-lane group addresses k-row
+        // k0 + i/4 (k0 = 16t + 8fk + 4r), columns c0 + 4(i%4), c0 = row block + 16((l/16)&1)
+        const int q = (lane & 15) >> 2;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = rb + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            o.rd[b] = (8 * fk + q) * ROWS * 2 + (((col >> 3) ^ (4 * q)) << 4) + (col & 7) * 2;
+        }
+    }
+}
+
+template <bool RC, int ROWS>
+__device__ __forceinline__ void operand_copy(const Operand& o, uint4* dst, int stage, int wave) {
+    constexpr int kInstr = ROWS / 64;
+    const int half = stage >= o.split ? 1 : 0;
+    const uint32_t soff0 = o.wfirst + static_cast<uint32_t>(stage - half * o.split) * o.kstep;
+#pragma unroll
+    for (int j = 0; j < kInstr; ++j) {
+        // LDS destination: this wave's j-th kilobyte of the tile
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(half ? o.res[1] : o.res[0], (lds_ptr_t)(dst + (wave * kInstr + j) * 64), 16,
+                                                 o.vo[j & 1], soff0 + j * o.jstep, 0, 0);
+    }
+}
+
+// The 8 k-consecutive bf16 of block b at k16 step t.
+template <bool RC, int ROWS>
+__device__ __forceinline__ bf16x8_t operand_frag(const Operand& o, const uint4* tile, int b, int t) {
+    if (!RC) {
+        const int off = o.rd[t] + b * 32 * 64;
+        return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + off));
+    } else {
+        lds_char_t base = (lds_char_t)(tile);
+        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(base + o.rd[b] + (16 * t) * ROWS * 2));
+        const v4s_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(base + o.rd[b] + (16 * t + 4) * ROWS * 2));
+        u32x4_t v;
+        v[0] = static_cast<uint16_t>(lo[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16);
+        v[1] = static_cast<uint16_t>(lo[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16);
+        v[2] = static_cast<uint16_t>(hi[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16);
+        v[3] = static_cast<uint16_t>(hi[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16);
+        return as_bf16x8(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The grouped GEMM
+// ---------------------------------------------------------------------------
+
+enum Epi { kEpiPreact = 0, kEpiGrad = 1, kEpiDx = 2, kEpiDw = 3 };
+
+struct GemmArgs {
+    // X (u operand): tile origin = x0 + (u0 or k0 rows) ...; see the tile set-up
+    const bf16_t* xa;       // first half
+    const bf16_t* xb;       // second half (split along u for k-contiguous X, along k for row-contiguous X)
+    int64_t x_estride;      // elements between experts (weights) or 0 (per-row data)
+    int ldx;
+    int xsplit;             // u (k-contiguous) or k (row-contiguous) where xb takes over; 0 = none
+    // Y (v operand)
+    const bf16_t* y;
+    int ldy;
+    // shape
+    int U, V, K;            // V or K = 0: taken from the expert segments
+    const int32_t* offsets; // [n + 1] expert segments of the permuted rows
+    int n_exp;
+    // outputs
+    void* c0;
+    void* c1;
+    int64_t c_estride;
+    int ldc;
+    int csplit;             // v where c1 takes over (kEpiDw), else 0
+    // kEpiGrad
+    const float* a;         // [P, 2F] pre-activations (fp32)
+    const float* gp;        // [P] gate of each row (0 for padding)
+    bf16_t* hg;             // [P, F]
+    float* dgp;             // [U / kTU, P] partial dg sums
+    int P;
+};
+
+template <bool XRC, bool YRC, int EPI, bool TOKEN_V>
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
+    __shared__ uint4 smem[2 * kStageVec];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int wu = wave & 1, wv = wave >> 1;
+    const int nut = g.U / kTU;
+
+    // ---- tile of this block: (expert e, u tile ut, v tile vt), XCD-aware
+    int e = 0, ut = 0, vt = 0, kbeg = 0, klen = g.K;
+    if (TOKEN_V) {
+        // v runs over the expert's rows: expert e owns nut * (len_e / kTV) tiles
+        int total = 0;
+        for (int j = 0; j < g.n_exp; ++j) total += (g.offsets[j + 1] - g.offsets[j]) / kTV * nut;
+        const int run = (total + 7) >> 3;
+        if (static_cast<int>(blockIdx.x >> 3) >= run) return;
+        int L = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
+        if (L >= total) return;
+        for (e = 0; e < g.n_exp; ++e) {
+            const int nv = (g.offsets[e + 1] - g.offsets[e]) / kTV;
+            if (L < nv * nut) {
+                ut = L / nv;
+                vt = L - ut * nv;
+                break;
+            }
+            L -= nv * nut;
+        }
+        vt = g.offsets[e] / kTV + vt;  // global v tile (row block of the permuted layout)
+    } else {
+        // fixed U x V per expert, K = the expert's rows
+        const int nvt = g.V / kTV;
+        const int total = g.n_exp * nut * nvt;
+        const int run = (total + 7) >> 3;
+        if (static_cast<int>(blockIdx.x >> 3) >= run) return;
+        const int L = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
+        if (L >= total) return;
+        e = L / (nut * nvt);
+        const int rem = L - e * nut * nvt;
+        ut = rem / nvt;
+        vt = rem - ut * nvt;
+        kbeg = g.offsets[e];
+        klen = g.offsets[e + 1] - kbeg;
+    }
+    const int u0 = ut * kTU, v0 = vt * kTV;
+    const int ns = klen / kBK;
+
+    // ---- operands
+    Operand ox;
+    Operand oy;
+    operand_setup<XRC, kTU>(ox, g.ldx, wave, lane);
+    operand_setup<YRC, kTV>(oy, g.ldy, wave, lane);
+    if (!XRC) {
+        // X rows u (weights [e][u][k]): the second half holds u >= xsplit
+        const bool second = g.xsplit > 0 && u0 >= g.xsplit;
+        const bf16_t* base = (second ? g.xb : g.xa) + e * g.x_estride +
+                             static_cast<int64_t>(u0 - (second ? g.xsplit : 0)) * g.ldx;
+        ox.res[0] = ox.res[1] = bwd_rsrc(base);
+        ox.split = 1 << 30;
+    } else if (TOKEN_V) {
+        // X = weights [e][k][u] (k = d or F rows), second half for k >= xsplit
+        ox.res[0] = bwd_rsrc(g.xa + e * g.x_estride + u0);
+        ox.res[1] = bwd_rsrc((g.xsplit > 0 ? g.xb : g.xa) + e * g.x_estride + u0);
+        ox.split = g.xsplit > 0 ? g.xsplit / kBK : (1 << 30);
+    } else {
+        // X = per-row data [p][u], k = the expert's rows
+        ox.res[0] = ox.res[1] = bwd_rsrc(g.xa + static_cast<int64_t>(kbeg) * g.ldx + u0);
+        ox.split = 1 << 30;
+    }
+    if (!YRC) {
+        // Y rows v = permuted rows [p][k]
+        oy.res[0] = oy.res[1] = bwd_rsrc(g.y + static_cast<int64_t>(v0) * g.ldy);
+    } else {
+        // Y = per-row data [p][v], k = the expert's rows
+        oy.res[0] = oy.res[1] = bwd_rsrc(g.y + static_cast<int64_t>(kbeg) * g.ldy + v0);
+    }
+    oy.split = 1 << 30;
+    operand_reads<XRC, kTU>(ox, wu * 128, lane);
+    operand_reads<YRC, kTV>(oy, wv * 64, lane);
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+        for (int bv = 0; bv < 2; ++bv)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[bu][bv][q] = 0.0f;
+
+    // ---- K loop.  Stage s: wait for its copies (every wave), read all of its
+    // fragments, then issue the copies of stage s+1 into the other buffer,
+    // then the MFMAs.  Reading before copying keeps the compiler's wait for
+    // the LDS writes of the copies (it cannot tell the two buffers apart) at
+    // the top of the next stage, so the copies overlap the MFMAs.
+    if (ns > 0) {
+        operand_copy<XRC, kTU>(ox, smem, 0, wave);
+        operand_copy<YRC, kTV>(oy, smem + kXVec, 0, wave);
+    }
+    for (int s = 0; s < ns; ++s) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this stage's copies have landed
+        __syncthreads();                     // ... for every wave; the other buffer is free
+        const uint4* cur = smem + (s & 1) * kStageVec;
+        bf16x8_t xf[2][4], yf[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) xf[t][b] = operand_frag<XRC, kTU>(ox, cur, b, t);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) yf[t][b] = operand_frag<YRC, kTV>(oy, cur + kXVec, b, t);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < ns) {
+            uint4* nxt = smem + ((s + 1) & 1) * kStageVec;
+            operand_copy<XRC, kTU>(ox, nxt, s + 1, wave);
+            operand_copy<YRC, kTV>(oy, nxt + kXVec, s + 1, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+                for (int bv = 0; bv < 2; ++bv)
+                    acc[bu][bv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[t][bu], yf[t][bv], acc[bu][bv], 0, 0, 0);
+    }
+
+    // ---- epilogue.  32x32 C layout: lane l holds column v = l%32 of each
+    // block and rows u = 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
+    const int fk = lane >> 5;
+    if (EPI == kEpiPreact || EPI == kEpiDx) {
+#pragma unroll
+        for (int bv = 0; bv < 2; ++bv) {
+            const int v = v0 + wv * 64 + bv * 32 + (lane & 31);
+#pragma unroll
+            for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int u = u0 + wu * 128 + bu * 32 + 8 * q4 + 4 * fk;
+                    const f32x16_t& c = acc[bu][bv];
+                    const f32x4_t o = {c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.c0) + static_cast<int64_t>(v) * g.ldc + u) = o;
+                }
+        }
+    } else if (EPI == kEpiDw) {
+        const bool second = g.csplit > 0 && v0 >= g.csplit;
+        float* cb = static_cast<float*>(second ? g.c1 : g.c0) + e * g.c_estride;
+        const int vb = v0 - (second ? g.csplit : 0);
+#pragma unroll
+        for (int bv = 0; bv < 2; ++bv) {
+            const int v = vb + wv * 64 + bv * 32 + (lane & 31);
+#pragma unroll
+            for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int u = u0 + wu * 128 + bu * 32 + 8 * q4 + 4 * fk;
+                    const f32x16_t& c = acc[bu][bv];
+                    const f32x4_t o = {c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
+                    *reinterpret_cast<f32x4_t*>(cb + static_cast<int64_t>(v) * g.ldc + u) = o;
+                }
+        }
+    } else {
+        // kEpiGrad: u = feature f of F, v = permuted row p.  With a1 = a[p][f],
+        // a3 = a[p][F + f], gate gv:  h = SiLU(a1) a3, dg += G h,
+        // da3 = gv G SiLU(a1), da1 = gv G a3 SiLU'(a1), hg = gv h.
+        const int F = g.U;
+        float dg[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int bv = 0; bv < 2; ++bv) {
+            const int p = v0 + wv * 64 + bv * 32 + (lane & 31);
+            const float gv = g.gp[p];
+            const float* arow = g.a + static_cast<int64_t>(p) * 2 * F;
+            bf16_t* darow = static_cast<bf16_t*>(g.c0) + static_cast<int64_t>(p) * 2 * F;
+            bf16_t* hrow = g.hg + static_cast<int64_t>(p) * F;
+#pragma unroll
+            for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int f = u0 + wu * 128 + bu * 32 + 8 * q4 + 4 * fk;
+                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(arow + f);
+                    const f32x4_t a3 = *reinterpret_cast<const f32x4_t*>(arow + F + f);
+                    float d1[4], d3[4], hv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float G = acc[bu][bv][4 * q4 + i];
+                        const float sg = sigmoid_f32(a1[i]);
+                        const float si = a1[i] * sg;
+                        const float h = si * a3[i];
+                        dg[bv] = fmaf(G, h, dg[bv]);
+                        const float dh = gv * G;
+                        d3[i] = dh * si;
+                        d1[i] = dh * a3[i] * (sg * (1.0f + a1[i] * (1.0f - sg)));
+                        hv[i] = gv * h;
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(d1[0], d1[1]);
+                    o.y = pack_bf16x2(d1[2], d1[3]);
+                    *reinterpret_cast<uint2*>(darow + f) = o;
+                    o.x = pack_bf16x2(d3[0], d3[1]);
+                    o.y = pack_bf16x2(d3[2], d3[3]);
+                    *reinterpret_cast<uint2*>(darow + F + f) = o;
+                    o.x = pack_bf16x2(hv[0], hv[1]);
+                    o.y = pack_bf16x2(hv[2], hv[3]);
+                    *reinterpret_cast<uint2*>(hrow + f) = o;
+                }
+        }
+        // dg partial over the block's 256 features, in a fixed order: the two
+        // k-group lanes of a column, then the two u halves of the block
+#pragma unroll
+        for (int bv = 0; bv < 2; ++bv) dg[bv] += __shfl_xor(dg[bv], 32, 64);
+        __syncthreads();  // the stage buffers are free
+        float* red = reinterpret_cast<float*>(smem);
+        if (fk == 0) {
+#pragma unroll
+            for (int bv = 0; bv < 2; ++bv) red[(wu * 2 + wv) * 64 + bv * 32 + lane] = dg[bv];
+        }
+        __syncthreads();
+        if (wu == 0 && fk == 0) {
+#pragma unroll
+            for (int bv = 0; bv < 2; ++bv) {
+                const int p = v0 + wv * 64 + bv * 32 + lane;
+                g.dgp[static_cast<int64_t>(ut) * g.P + p] =
+                    red[(0 * 2 + wv) * 64 + bv * 32 + lane] + red[(1 * 2 + wv) * 64 + bv * 32 + lane];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row gathers, router gradient, dx and dW_g
+// ---------------------------------------------------------------------------
+
+// xp[p] = x[t], dyp[p] = dy[t], gp[p] = gate of assignment a = row_src[p]
+// (t = a / K); zeros for padding rows.
+__global__ __launch_bounds__(256) void bwd_gather_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy,
+                                                         const float* __restrict__ gate,
+                                                         const int32_t* __restrict__ row_src, int d, int K,
+                                                         int n_src, bf16_t* __restrict__ xp, bf16_t* __restrict__ dyp,
+                                                         float* __restrict__ gp) {
+    const int p = blockIdx.x;
+    const int a = row_src[p];
+    const bool real = a >= 0 && a < n_src;
+    const int t = real ? a / K : 0;
+    const uint4* xs = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * d);
+    const uint4* ds = reinterpret_cast<const uint4*>(dy + static_cast<int64_t>(t) * d);
+    uint4* xo = reinterpret_cast<uint4*>(xp + static_cast<int64_t>(p) * d);
+    uint4* dout = reinterpret_cast<uint4*>(dyp + static_cast<int64_t>(p) * d);
+    for (int c = threadIdx.x; c < d / 8; c += 256) {
+        uint4 xv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
+        if (real) {
+            xv = xs[c];
+            dv = ds[c];
+        }
+        xo[c] = xv;
+        dout[c] = dv;
+    }
+    if (threadIdx.x == 0) gp[p] = real ? gate[a] : 0.0f;
+}
+
+// dl[t, :]: zero except the K selected experts, dl_s = g_s (dg_s - sum_j g_j dg_j),
+// dg_s = the sum of the row's partials over the nut feature tiles, in tile order.
+__global__ __launch_bounds__(256) void bwd_router_kernel(const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ gate,
+                                                         const int32_t* __restrict__ row_of,
+                                                         const float* __restrict__ dgp, int nut, int P, int T,
+                                                         int n, int K, float* __restrict__ dl) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    float dg[kMaxTopK], gs[kMaxTopK];
+    float S = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        dg[s] = 0.0f;
+        gs[s] = 0.0f;
+        if (s < K) {
+            const int p = row_of[t * K + s];
+            if (p >= 0)
+                for (int u = 0; u < nut; ++u) dg[s] += dgp[static_cast<int64_t>(u) * P + p];
+            gs[s] = gate[t * K + s];
+            S = fmaf(gs[s], dg[s], S);
+        }
+    }
+    float* row = dl + static_cast<int64_t>(t) * n;
+    for (int e = 0; e < n; ++e) row[e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+        if (s < K) row[idx[t * K + s]] = gs[s] * (dg[s] - S);
+}
+
+// dx[t] = sum_s dxp[row_of[t, s]] (slot order) + sum_s dl[t, e_s] W_g[:, e_s], one rounding to bf16.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ row_of,
+                                                     const int32_t* __restrict__ idx, const float* __restrict__ dl,
+                                                     const float* __restrict__ wg, int d, int n, int K,
+                                                     bf16_t* __restrict__ dx) {
+    const int t = blockIdx.x;
+    int p[kMaxTopK], es[kMaxTopK];
+    float ls[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        p[s] = s < K ? row_of[t * K + s] : -1;
+        es[s] = s < K ? idx[t * K + s] : 0;
+        ls[s] = s < K ? dl[static_cast<int64_t>(t) * n + es[s]] : 0.0f;
+    }
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (s < K && p[s] >= 0) {
+                const float4 a = reinterpret_cast<const float4*>(dxp + static_cast<int64_t>(p[s]) * d)[c];
+                v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (s < K) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = fmaf(ls[s], wg[static_cast<int64_t>(4 * c + i) * n + es[s]], v[i]);
+            }
+        }
+        uint2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(dx + static_cast<int64_t>(t) * d + 4 * c) = o;
+    }
+}
+
+constexpr int kDwgTokens = 64;  // tokens per partial sum of dW_g
+
+// part[chunk][k][e] = sum over the chunk's tokens of x[t][k] dl[t][e]
+__global__ __launch_bounds__(256) void bwd_dwg_partial_kernel(const bf16_t* __restrict__ x,
+                                                              const float* __restrict__ dl, int T, int d, int n,
+                                                              float* __restrict__ part) {
+    __shared__ float s_dl[kDwgTokens * kMaxExperts];
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    const int t0 = blockIdx.y * kDwgTokens;
+    const int nt = min(kDwgTokens, T - t0);
+    for (int i = threadIdx.x; i < nt * n; i += 256) s_dl[i] = dl[static_cast<int64_t>(t0) * n + i];
+    __syncthreads();
+    if (k >= d) return;
+    float acc[kMaxExperts];
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) acc[e] = 0.0f;
+    for (int i = 0; i < nt; ++i) {
+        const float xv = bf16_to_f32(x[static_cast<int64_t>(t0 + i) * d + k]);
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e)
+            if (e < n) acc[e] = fmaf(xv, s_dl[i * n + e], acc[e]);
+    }
+    float* out = part + (static_cast<int64_t>(blockIdx.y) * d + k) * n;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e)
+        if (e < n) out[e] = acc[e];
+}
+
+__global__ __launch_bounds__(256) void bwd_dwg_reduce_kernel(const float* __restrict__ part, int chunks, int dn,
+                                                             float* __restrict__ dwg) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= dn) return;
+    float s = 0.0f;
+    for (int c = 0; c < chunks; ++c) s += part[static_cast<int64_t>(c) * dn + i];
+    dwg[i] = s;
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = 0.0f;
+}
+
+template <bool XRC, bool YRC, int EPI, bool TOKEN_V>
+hipError_t launch_gemm(const GemmArgs& g, int grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    bwd_gemm_kernel<XRC, YRC, EPI, TOKEN_V><<<grid, 256, 0, st>>>(g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Shape& s, BackwardWs* w, char* base) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base == nullptr ? nullptr : base + off;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    const size_t TK = static_cast<size_t>(s.T) * s.K;
+    const size_t P = TK + static_cast<size_t>(s.n) * (kTV - 1);
+    const size_t nut = static_cast<size_t>(s.F) / kTU;
+    const size_t chunks = (static_cast<size_t>(s.T) + kDwgTokens - 1) / kDwgTokens;
+    BackwardWs v{};
+    v.idx = reinterpret_cast<int32_t*>(take(TK * 4));
+    v.gate = reinterpret_cast<float*>(take(TK * 4));
+    v.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(s.n) * 4));
+    v.offsets = reinterpret_cast<int32_t*>(take(static_cast<size_t>(s.n + 1) * 4));
+    v.row_src = reinterpret_cast<int32_t*>(take(P * 4));
+    v.row_of = reinterpret_cast<int32_t*>(take(TK * 4));
+    v.xp = reinterpret_cast<bf16_t*>(take(P * s.d * 2));
+    v.dyp = reinterpret_cast<bf16_t*>(take(P * s.d * 2));
+    v.gp = reinterpret_cast<float*>(take(P * 4));
+    v.a = reinterpret_cast<float*>(take(P * 2 * s.F * 4));
+    v.da = reinterpret_cast<bf16_t*>(take(P * 2 * s.F * 2));
+    v.hg = reinterpret_cast<bf16_t*>(take(P * s.F * 2));
+    v.dgp = reinterpret_cast<float*>(take(nut * P * 4));
+    v.dxp = reinterpret_cast<float*>(take(P * s.d * 4));
+    v.dl = reinterpret_cast<float*>(take(static_cast<size_t>(s.T) * s.n * 4));
+    v.dwg_part = reinterpret_cast<float*>(take(chunks * s.d * s.n * 4));
+    v.P = static_cast<int>(P);
+    if (w != nullptr) *w = v;
+    return off;
+}
+
+bool backward_fits(const Shape& s) {
+    // 32-bit offsets: the per-row buffers (the largest, a: P x 2F fp32) and
+    // the weights of one expert must stay below 2 GiB
+    const long long P = static_cast<long long>(s.T) * s.K + static_cast<long long>(s.n) * (kTV - 1);
+    return P * 2LL * s.F * 4 < (1LL << 31) && 2LL * s.F * s.d * 2 < (1LL << 31) && s.F % kTU == 0 &&
+           s.d % kTU == 0;
+}
+
+hipError_t launch_zero_grads(const Shape& s, float* dwg, float* dw1, float* dw3, float* dw2, hipStream_t st) {
+    const int64_t nw = static_cast<int64_t>(s.n) * s.F * s.d;
+    bwd_zero_kernel<<<1024, 256, 0, st>>>(dw1, nw);
+    bwd_zero_kernel<<<1024, 256, 0, st>>>(dw3, nw);
+    bwd_zero_kernel<<<1024, 256, 0, st>>>(dw2, nw);
+    bwd_zero_kernel<<<16, 256, 0, st>>>(dwg, static_cast<int64_t>(s.d) * s.n);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg, const void* w1, const void* w3,
+                                 const void* w2, const void* dy, void* dx, float* dwg, float* dw1, float* dw3,
+                                 float* dw2, const BackwardWs& w, hipStream_t st) {
+    hipError_t err;
+    const int d = s.d, F = s.F, n = s.n, K = s.K, T = s.T;
+    const int P = w.P;
+    const int TK = T * K;
+    const auto* xb = static_cast<const bf16_t*>(x);
+    const auto* w1b = static_cast<const bf16_t*>(w1);
+    const auto* w3b = static_cast<const bf16_t*>(w3);
+    const auto* w2b = static_cast<const bf16_t*>(w2);
+    if ((err = launch_router_topk(s, x, wg, w.idx, w.gate, nullptr, st)) != hipSuccess) return err;
+    if ((err = launch_permute(s, kTV, w.idx, w.counts, w.offsets, w.row_src, w.row_of, st)) != hipSuccess) return err;
+    bwd_gather_kernel<<<P, 256, 0, st>>>(xb, static_cast<const bf16_t*>(dy), w.gate, w.row_src, d, K, TK, w.xp, w.dyp,
+                                          w.gp);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    const int vmax = (P + kTV - 1) / kTV;  // worst-case row tiles
+    auto grid8 = [](long long tiles) { return static_cast<int>((tiles + 7) / 8 * 8); };
+
+    // 1. a = [a1 | a3]: X = [w1; w3] rows (k-contiguous), Y = xp rows
+    GemmArgs g{};
+    g.xa = w1b; g.xb = w3b; g.x_estride = static_cast<int64_t>(F) * d; g.ldx = d; g.xsplit = F;
+    g.y = w.xp; g.ldy = d;
+    g.U = 2 * F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;
+    g.c0 = w.a; g.ldc = 2 * F; g.P = P;
+    if ((err = launch_gemm<false, false, kEpiPreact, true>(g, grid8(static_cast<long long>(2 * F / kTU) * vmax), st)) !=
+        hipSuccess)
+        return err;
+
+    // 2. G = dyp . w2 with the gradient epilogue: X = w2[e] as [k = d][u = F]
+    g = GemmArgs{};
+    g.xa = w2b; g.xb = w2b; g.x_estride = static_cast<int64_t>(d) * F; g.ldx = F; g.xsplit = 0;
+    g.y = w.dyp; g.ldy = d;
+    g.U = F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;
+    g.c0 = w.da; g.ldc = 2 * F;
+    g.a = w.a; g.gp = w.gp; g.hg = w.hg; g.dgp = w.dgp; g.P = P;
+    if ((err = launch_gemm<true, false, kEpiGrad, true>(g, grid8(static_cast<long long>(F / kTU) * vmax), st)) !=
+        hipSuccess)
+        return err;
+
+    // 3. dxp = da . [w1; w3]: X = w1[e] (k < F) then w3[e], as [k][u = d]
+    g = GemmArgs{};
+    g.xa = w1b; g.xb = w3b; g.x_estride = static_cast<int64_t>(F) * d; g.ldx = d; g.xsplit = F;
+    g.y = w.da; g.ldy = 2 * F;
+    g.U = d; g.V = 0; g.K = 2 * F; g.offsets = w.offsets; g.n_exp = n;
+    g.c0 = w.dxp; g.ldc = d; g.P = P;
+    if ((err = launch_gemm<true, false, kEpiDx, true>(g, grid8(static_cast<long long>(d / kTU) * vmax), st)) !=
+        hipSuccess)
+        return err;
+
+    // 4. dw2[e][j][f] = sum_p hg[p][f] dyp[p][j]: u = f, v = j
+    g = GemmArgs{};
+    g.xa = w.hg; g.xb = w.hg; g.ldx = F;
+    g.y = w.dyp; g.ldy = d;
+    g.U = F; g.V = d; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
+    g.c0 = dw2; g.c1 = dw2; g.c_estride = static_cast<int64_t>(d) * F; g.ldc = F; g.csplit = 0; g.P = P;
+    if ((err = launch_gemm<true, true, kEpiDw, false>(
+             g, grid8(static_cast<long long>(n) * (F / kTU) * (d / kTV)), st)) != hipSuccess)
+        return err;
+
+    // 5. dw1/dw3[e][f][j] = sum_p da[p][f'] xp[p][j]: u = j, v = f' (f' >= F: dw3)
+    g = GemmArgs{};
+    g.xa = w.xp; g.xb = w.xp; g.ldx = d;
+    g.y = w.da; g.ldy = 2 * F;
+    g.U = d; g.V = 2 * F; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
+    g.c0 = dw1; g.c1 = dw3; g.c_estride = static_cast<int64_t>(F) * d; g.ldc = d; g.csplit = F; g.P = P;
+    if ((err = launch_gemm<true, true, kEpiDw, false>(
+             g, grid8(static_cast<long long>(n) * (d / kTU) * (2 * F / kTV)), st)) != hipSuccess)
+        return err;
+
+    // router gradient, dx, dW_g
+    bwd_router_kernel<<<(T + 255) / 256, 256, 0, st>>>(w.idx, w.gate, w.row_of, w.dgp, F / kTU, P, T, n, K, w.dl);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    bwd_dx_kernel<<<T, 256, 0, st>>>(w.dxp, w.row_of, w.idx, w.dl, wg, d, n, K, static_cast<bf16_t*>(dx));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int chunks = (T + kDwgTokens - 1) / kDwgTokens;
+    bwd_dwg_partial_kernel<<<dim3((d + 255) / 256, chunks), 256, 0, st>>>(xb, w.dl, T, d, n, w.dwg_part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    bwd_dwg_reduce_kernel<<<(d * n + 255) / 256, 256, 0, st>>>(w.dwg_part, chunks, d * n, dwg);
+    return hipGetLastError();
+}
+
+}  // namespace moe

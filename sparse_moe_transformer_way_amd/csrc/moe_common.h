@@ -57,6 +57,12 @@ __device__ __forceinline__ float silu_f32(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
 }
 
+// sigma(z) = 1 / (1 + exp(-z)), with the same hardware exp2 and reciprocal.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
+}
+
 // ---------------------------------------------------------------------------
 // Internal launchers (host side).  Each enqueues on `stream` and returns the
 // hipGetLastError() status of its launches.  Shapes are validated by the ABI.
@@ -97,6 +103,34 @@ hipError_t launch_down_fp8(const Shape& s, const void* h, const int32_t* counts,
                            const uint8_t* w2, const float* s2, float* y_perm, hipStream_t st);
 // Per-row E4M3 quantization of a bf16 [rows, cols] matrix (cols % 8 == 0).
 hipError_t launch_quantize_fp8(int64_t rows, int cols, const void* w, uint8_t* q, float* scale, hipStream_t st);
+
+// Backward pass (bf16).  Workspace pieces, carved by backward_workspace_bytes
+// (base == nullptr only sizes it).  Rows are padded to 128 per expert.
+struct BackwardWs {
+    int32_t* idx;
+    float* gate;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* row_src;
+    int32_t* row_of;
+    bf16_t* xp;       // [P, d] gathered x
+    bf16_t* dyp;      // [P, d] gathered dy
+    float* gp;        // [P] gate of each row
+    float* a;         // [P, 2F] pre-activations a1 | a3
+    bf16_t* da;       // [P, 2F] their gradients
+    bf16_t* hg;       // [P, F] gate * h
+    float* dgp;       // [F / 256, P] partial gate gradients
+    float* dxp;       // [P, d] per-row input gradients
+    float* dl;        // [T, n] router logit gradients
+    float* dwg_part;  // [ceil(T / 64), d, n]
+    int P;
+};
+size_t backward_workspace_bytes(const Shape& s, BackwardWs* w, char* base);
+bool backward_fits(const Shape& s);
+hipError_t launch_zero_grads(const Shape& s, float* dwg, float* dw1, float* dw3, float* dw2, hipStream_t st);
+hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg, const void* w1, const void* w3,
+                                 const void* w2, const void* dy, void* dx, float* dwg, float* dw1, float* dw3,
+                                 float* dw2, const BackwardWs& w, hipStream_t st);
 
 // Whether the tiled kernels can address this shape's token rows (gate/up
 // reaches the rows of x through 32-bit byte offsets: T * d_model * 2 bytes

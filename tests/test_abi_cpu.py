@@ -180,3 +180,27 @@ def test_quantize_fp8_argument_checks():
     assert lib.moe_quantize_fp8(10, 16, FAKE, FAKE + 4, FAKE, None) == 1    # q alignment
     assert lib.moe_quantize_fp8(10, 16, FAKE, FAKE, None, None) == 1
     assert lib.moe_quantize_fp8(0, 16, None, None, None, None) == 0
+
+
+def test_backward_descriptor_rules():
+    """The backward pass takes bf16 layers only; argument checks come before
+    any launch."""
+    assert moe.moe_backward_workspace_size(D(), 4096) > 0
+    assert moe.moe_backward_workspace_size(D(act_dtype=0, weight_dtype=0, d_model=512, d_ffn=512), 64) == 0
+    assert moe.moe_backward_workspace_size(D(weight_dtype=2), 64) == 0
+    assert moe.moe_backward_workspace_size(D(), -1) == 0
+    assert moe.moe_backward_workspace_size(D(), 1 << 20) == 0   # per-row buffers past 2 GiB
+    lib = _lib.lib
+    f32 = ctypes.byref(D(act_dtype=0, weight_dtype=0, d_model=512, d_ffn=512))
+    args = [FAKE] * 11
+    assert lib.moe_layer_backward(f32, 4, *args, FAKE, 1 << 30, None) == 2
+    pb = ctypes.byref(D())
+    assert lib.moe_layer_backward(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                  FAKE, 1 << 40, None) == 1          # no dw_gate
+    assert lib.moe_layer_backward(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, 1 << 40, None) == 1          # dx aliases x
+    assert lib.moe_layer_backward(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4096, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE + 16, 1 << 40, None) == 1  # workspace not 256-aligned
+    assert lib.moe_layer_backward(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4096, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, 10, None) == 3         # workspace too small
+    assert lib.moe_layer_backward(pb, -1, *args, FAKE, 1 << 30, None) == 1

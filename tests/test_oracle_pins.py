@@ -570,3 +570,18 @@ def test_backward_top1_closed_form():
         sel = g["idx"][:, 0] == e
         h = (x[sel] @ w1[e].T) * (1 / (1 + np.exp(-(x[sel] @ w1[e].T)))) * (x[sel] @ w3[e].T)
         np.testing.assert_allclose(g["dw2"][e], dy[sel].T @ h, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_sampled_helpers_match_dense():
+    """The per-token and per-expert-row backward helpers (used on full-size
+    layers) agree with the dense backward oracle."""
+    x, wg, w1, w3, w2, dy = _bwd_case(51, T=20, d=16, F=24, n=6, K=2)
+    g = oracle.moe_layer_backward(x, wg, w1, w3, w2, dy, K=2)
+    tok = np.array([0, 3, 7, 19])
+    r = oracle.backward_token_rows(x, wg, w1, w3, w2, dy, tok, K=2)
+    np.testing.assert_allclose(r["dx"], g["dx"][tok], rtol=1e-12, atol=1e-12)
+    for e in range(6):
+        rows = oracle.backward_expert_rows(x, wg, w1, w3, w2, dy, e, [0, 5, 23], [1, 15], K=2)
+        np.testing.assert_allclose(rows["dw1"], g["dw1"][e][[0, 5, 23]], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rows["dw3"], g["dw3"][e][[0, 5, 23]], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rows["dw2"], g["dw2"][e][[1, 15]], rtol=1e-12, atol=1e-12)
