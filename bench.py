@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer tokens/s on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny|decode_fp8]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny|decode_fp8|backward]
 
 One step is one pass of the whole layer (router -> permute -> gate/up + SwiGLU ->
 down -> combine) over one batch of synthetic tokens already resident in HBM.
@@ -11,7 +11,9 @@ points with HIP events around each stage, recorded on the stream the kernels
 run on, which gives each kernel's average duration for the roofline figure.
 The CPU oracle is then timed on a bounded sample of the same workload.
 decode_fp8 is the decode workload with its expert weights quantized to FP8
-(E4M3, one scale per row) on the device before any timing.
+(E4M3, one scale per row) on the device before any timing.  backward times
+moe_layer_backward (all gradients of the layer) on the prefill workload's
+inputs with a seeded upstream gradient; its roofline covers the whole pass.
 
 Prints one JSON line.  Only one GPU is used; --gpus above 1 is refused.
 """
@@ -29,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X + % of HBM (decode) / MFMA (prefill) roofline"
-WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3, "decode_fp8": 1}
+WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3, "decode_fp8": 1, "backward": 2}
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
@@ -107,6 +109,71 @@ def cpu_baseline(inp, seconds: float, rows_cap: int):
                       f"{done // rows.size} calls in {el:.1f} s"}
 
 
+def bench_backward(args, inp, spec):
+    """Steps of moe_layer_backward between device synchronisations, then the
+    same steps between HIP events on the launch stream."""
+    import torch
+    import sparse_moe_transformer_way_amd as moe
+
+    T, d, F, n, K = inp.T, inp.d, inp.F, inp.n, inp.K
+    dev = torch.device("cuda")
+    x, wg, w1, w3, w2 = (t.to(dev) for t in (inp.x, inp.wg, inp.w1, inp.w3, inp.w2))
+    gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
+    dy = torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16)
+    desc = moe.make_desc(d, F, n, K)
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    dwg = torch.empty((d, n), dtype=torch.float32, device=dev)
+    dw1 = torch.empty((n, F, d), dtype=torch.float32, device=dev)
+    dw3 = torch.empty((n, F, d), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((n, d, F), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_backward_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer_backward(desc, x, wg, w1, w3, w2, dy, dx, dwg, dw1, dw3, dw2, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ev_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    TK = T * K
+    # five grouped products of 2 * TK * d * F flop each, two of them doubled (w1 and w3)
+    flops = 16.0 * TK * d * F
+    achieved = flops / (ev_ms / 1e3) / 1e12
+    out = {
+        "metric": "MoE-layer backward tokens/sec at 1 MI355X + % of MFMA roofline",
+        "value": round(T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec["name"] + "_backward", "T": T, "d_model": d, "d_ffn": F, "n_experts": n,
+                   "top_k": K, "weight_grads": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_layer_backward (all kernels of the pass)", "kernel_ms": round(ev_ms, 4),
+                     "algorithmic_per_launch": flops},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -125,6 +192,9 @@ def main():
     wl = WORKLOADS[args.workload]
     spec = mi.WORKLOADS[wl]
     inp = mi.make_workload(wl, seed=args.seed)
+    if args.workload == "backward":
+        bench_backward(args, inp, spec)
+        return
     T, d, F, n, K = inp.T, inp.d, inp.F, inp.n, inp.K
     dt = torch.float32 if inp.dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda")
