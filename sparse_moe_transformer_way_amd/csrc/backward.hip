@@ -16,7 +16,7 @@
 //
 // The pass recomputes the routing and the gate/up pre-activations a1, a3
 // (nothing of the forward pass is kept), then runs five grouped GEMMs through
-// one MFMA kernel, over the expert-grouped rows padded to 128:
+// one MFMA kernel, over the expert-grouped rows padded to 256:
 //   1. a = [a1 | a3] = xp . [w1; w3]^T       u = 2F features, v = rows, K = d (fp32)
 //   2. G = dyp . w2                           u = F, v = rows, K = d; epilogue
 //      forms h, dg partial sums, da = [da1 | da3] and hg = g h
@@ -40,11 +40,21 @@ namespace moe {
 namespace {
 
 constexpr int kTU = 256;  // block tile along u (MFMA rows)
-constexpr int kTV = 128;  // block tile along v (MFMA columns); row padding of the layout
+constexpr int kTV = 256;  // block tile along v (MFMA columns); row padding of the layout
 constexpr int kBK = 32;   // k per stage
 constexpr int kXVec = kTU * kBK * 2 / 16;  // uint4 of an X stage (16 KB)
-constexpr int kYVec = kTV * kBK * 2 / 16;  // uint4 of a Y stage (8 KB)
+constexpr int kYVec = kTV * kBK * 2 / 16;  // uint4 of a Y stage (16 KB)
 constexpr int kStageVec = kXVec + kYVec;
+constexpr int kStages = 4;                 // LDS ring: copies run kStages - 1 stages ahead
+constexpr int kCopiesPerStage = (kTU + kTV) / 64;  // buffer loads per thread per stage
+
+// Wait until at most N of this wave's buffer loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at their maximum
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
 
 typedef void __attribute__((address_space(3)))* lds_ptr_t;
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -173,6 +183,75 @@ __device__ __forceinline__ bf16x8_t operand_frag(const Operand& o, const uint4* 
 // The grouped GEMM
 // ---------------------------------------------------------------------------
 
+typedef bf16x8_t StageFrags[2][4];  // [k16 step][32-row block]
+
+template <bool XRC, bool YRC>
+__device__ __forceinline__ void read_stage(const Operand& ox, const Operand& oy, const uint4* cur, StageFrags& xf,
+                                           StageFrags& yf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xf[t][b] = operand_frag<XRC, kTU>(ox, cur, b, t);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) yf[t][b] = operand_frag<YRC, kTV>(oy, cur + kXVec, b, t);
+    }
+}
+
+__device__ __forceinline__ void mfma_stage(const StageFrags& xf, const StageFrags& yf, f32x16_t (&acc)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+            for (int bv = 0; bv < 4; ++bv)
+                acc[bu][bv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[t][bu], yf[t][bv], acc[bu][bv], 0, 0, 0);
+}
+
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
+constexpr int kSchedDsRead = 0x100;
+
+// Issue order of one stage: an MFMA then a fragment read of the next stage,
+// NREAD times; the next copies; the remaining MFMAs.
+template <int NREAD>
+__device__ __forceinline__ void sched_stage() {
+#pragma unroll
+    for (int u = 0; u < NREAD; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedVmem, kCopiesPerStage, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 32 - NREAD, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stage s of the K loop.  The ring's four stage buffers are distinct LDS
+// arrays, so the compiler's own wait before an LDS read covers only the copies
+// into the buffer it reads.  On entry `cx`, `cy` hold stage s's fragments
+// (reads in flight at most).  NEXT: wait until stage s+1 has landed for every
+// wave (the copies of stage s+2 stay in flight), read it from `rd` into `nx`,
+// `ny`, copy stage min(s+3, ns-1) into `cp` (the buffer of stage s-1, which
+// every wave finished with before this barrier; a repeated last stage only
+// refills a free buffer and keeps the count of copies in flight uniform),
+// then the MFMAs of stage s, interleaved with those reads.
+template <bool XRC, bool YRC, bool NEXT>
+__device__ __forceinline__ void k_stage(const Operand& ox, const Operand& oy, const uint4* rd, uint4* cp, int s,
+                                        int ns, int wave, const StageFrags& cx, const StageFrags& cy, StageFrags& nx,
+                                        StageFrags& ny, f32x16_t (&acc)[4][4]) {
+    constexpr int kRead = (XRC ? 16 : 8) + (YRC ? 16 : 8);  // LDS read instructions per stage
+    if (NEXT) {
+        wait_vm<kCopiesPerStage>();
+        // a bare barrier: __syncthreads() would also wait for the copies in flight
+        __builtin_amdgcn_s_barrier();
+        read_stage<XRC, YRC>(ox, oy, rd, nx, ny);
+        const int sn = min(s + kStages - 1, ns - 1);
+        operand_copy<XRC, kTU>(ox, cp, sn, wave);
+        operand_copy<YRC, kTV>(oy, cp + kXVec, sn, wave);
+    }
+    mfma_stage(cx, cy, acc);
+    if (NEXT) sched_stage<kRead>();
+}
+
 enum Epi { kEpiPreact = 0, kEpiGrad = 1, kEpiDx = 2, kEpiDw = 3 };
 
 struct GemmArgs {
@@ -204,8 +283,13 @@ struct GemmArgs {
 };
 
 template <bool XRC, bool YRC, int EPI, bool TOKEN_V>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
-    __shared__ uint4 smem[2 * kStageVec];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_gemm_kernel(GemmArgs g) {
+    static_assert(kStages == 4, "the K loop is unrolled over a ring of four buffers");
+    __shared__ uint4 sb0[kStageVec];
+    __shared__ uint4 sb1[kStageVec];
+    __shared__ uint4 sb2[kStageVec];
+    __shared__ uint4 sb3[kStageVec];
+    uint4* const smem = sb0;  // the epilogue's reduction space
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -281,51 +365,45 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
     }
     oy.split = 1 << 30;
     operand_reads<XRC, kTU>(ox, wu * 128, lane);
-    operand_reads<YRC, kTV>(oy, wv * 64, lane);
+    operand_reads<YRC, kTV>(oy, wv * 128, lane);
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[4][4];
 #pragma unroll
     for (int bu = 0; bu < 4; ++bu)
 #pragma unroll
-        for (int bv = 0; bv < 2; ++bv)
+        for (int bv = 0; bv < 4; ++bv)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[bu][bv][q] = 0.0f;
 
-    // ---- K loop.  Stage s: wait for its copies (every wave), read all of its
-    // fragments, then issue the copies of stage s+1 into the other buffer,
-    // then the MFMAs.  Reading before copying keeps the compiler's wait for
-    // the LDS writes of the copies (it cannot tell the two buffers apart) at
-    // the top of the next stage, so the copies overlap the MFMAs.
+    // ---- K loop over a ring of four LDS buffers, copies three stages ahead;
+    // each stage's MFMAs overlap the next stage's fragment reads.  ns is a
+    // multiple of 8 (K is d, 2F or a segment length: multiples of 256), so the
+    // loop runs in groups of four stages and the last group is peeled: no
+    // branch carries the accumulators.
     if (ns > 0) {
-        operand_copy<XRC, kTU>(ox, smem, 0, wave);
-        operand_copy<YRC, kTV>(oy, smem + kXVec, 0, wave);
-    }
-    for (int s = 0; s < ns; ++s) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this stage's copies have landed
-        __syncthreads();                     // ... for every wave; the other buffer is free
-        const uint4* cur = smem + (s & 1) * kStageVec;
-        bf16x8_t xf[2][4], yf[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) xf[t][b] = operand_frag<XRC, kTU>(ox, cur, b, t);
-#pragma unroll
-            for (int b = 0; b < 2; ++b) yf[t][b] = operand_frag<YRC, kTV>(oy, cur + kXVec, b, t);
+        operand_copy<XRC, kTU>(ox, sb0, 0, wave);
+        operand_copy<YRC, kTV>(oy, sb0 + kXVec, 0, wave);
+        operand_copy<XRC, kTU>(ox, sb1, 1, wave);
+        operand_copy<YRC, kTV>(oy, sb1 + kXVec, 1, wave);
+        operand_copy<XRC, kTU>(ox, sb2, 2, wave);
+        operand_copy<YRC, kTV>(oy, sb2 + kXVec, 2, wave);
+        StageFrags xa, ya, xb, yb;
+        wait_vm<2 * kCopiesPerStage>();
+        __builtin_amdgcn_s_barrier();
+        read_stage<XRC, YRC>(ox, oy, sb0, xa, ya);
+        int s = 0;
+        for (; s + 4 < ns; s += 4) {
+            k_stage<XRC, YRC, true>(ox, oy, sb1, sb3, s, ns, wave, xa, ya, xb, yb, acc);
+            k_stage<XRC, YRC, true>(ox, oy, sb2, sb0, s + 1, ns, wave, xb, yb, xa, ya, acc);
+            k_stage<XRC, YRC, true>(ox, oy, sb3, sb1, s + 2, ns, wave, xa, ya, xb, yb, acc);
+            k_stage<XRC, YRC, true>(ox, oy, sb0, sb2, s + 3, ns, wave, xb, yb, xa, ya, acc);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < ns) {
-            uint4* nxt = smem + ((s + 1) & 1) * kStageVec;
-            operand_copy<XRC, kTU>(ox, nxt, s + 1, wave);
-            operand_copy<YRC, kTV>(oy, nxt + kXVec, s + 1, wave);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int bu = 0; bu < 4; ++bu)
-#pragma unroll
-                for (int bv = 0; bv < 2; ++bv)
-                    acc[bu][bv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[t][bu], yf[t][bv], acc[bu][bv], 0, 0, 0);
+        k_stage<XRC, YRC, true>(ox, oy, sb1, sb3, s, ns, wave, xa, ya, xb, yb, acc);
+        k_stage<XRC, YRC, true>(ox, oy, sb2, sb0, s + 1, ns, wave, xb, yb, xa, ya, acc);
+        k_stage<XRC, YRC, true>(ox, oy, sb3, sb1, s + 2, ns, wave, xa, ya, xb, yb, acc);
+        k_stage<XRC, YRC, false>(ox, oy, sb0, sb2, s + 3, ns, wave, xb, yb, xa, ya, acc);
+        wait_vm<0>();  // the repeated tail copies, before the LDS is reused
+        __builtin_amdgcn_s_barrier();
     }
 
     // ---- epilogue.  32x32 C layout: lane l holds column v = l%32 of each
@@ -333,8 +411,8 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
     const int fk = lane >> 5;
     if (EPI == kEpiPreact || EPI == kEpiDx) {
 #pragma unroll
-        for (int bv = 0; bv < 2; ++bv) {
-            const int v = v0 + wv * 64 + bv * 32 + (lane & 31);
+        for (int bv = 0; bv < 4; ++bv) {
+            const int v = v0 + wv * 128 + bv * 32 + (lane & 31);
 #pragma unroll
             for (int bu = 0; bu < 4; ++bu)
 #pragma unroll
@@ -350,8 +428,8 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
         float* cb = static_cast<float*>(second ? g.c1 : g.c0) + e * g.c_estride;
         const int vb = v0 - (second ? g.csplit : 0);
 #pragma unroll
-        for (int bv = 0; bv < 2; ++bv) {
-            const int v = vb + wv * 64 + bv * 32 + (lane & 31);
+        for (int bv = 0; bv < 4; ++bv) {
+            const int v = vb + wv * 128 + bv * 32 + (lane & 31);
 #pragma unroll
             for (int bu = 0; bu < 4; ++bu)
 #pragma unroll
@@ -367,10 +445,10 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
         // a3 = a[p][F + f], gate gv:  h = SiLU(a1) a3, dg += G h,
         // da3 = gv G SiLU(a1), da1 = gv G a3 SiLU'(a1), hg = gv h.
         const int F = g.U;
-        float dg[2] = {0.0f, 0.0f};
+        float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int bv = 0; bv < 2; ++bv) {
-            const int p = v0 + wv * 64 + bv * 32 + (lane & 31);
+        for (int bv = 0; bv < 4; ++bv) {
+            const int p = v0 + wv * 128 + bv * 32 + (lane & 31);
             const float gv = g.gp[p];
             const float* arow = g.a + static_cast<int64_t>(p) * 2 * F;
             bf16_t* darow = static_cast<bf16_t*>(g.c0) + static_cast<int64_t>(p) * 2 * F;
@@ -410,20 +488,20 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(GemmArgs g) {
         // dg partial over the block's 256 features, in a fixed order: the two
         // k-group lanes of a column, then the two u halves of the block
 #pragma unroll
-        for (int bv = 0; bv < 2; ++bv) dg[bv] += __shfl_xor(dg[bv], 32, 64);
+        for (int bv = 0; bv < 4; ++bv) dg[bv] += __shfl_xor(dg[bv], 32, 64);
         __syncthreads();  // the stage buffers are free
         float* red = reinterpret_cast<float*>(smem);
         if (fk == 0) {
 #pragma unroll
-            for (int bv = 0; bv < 2; ++bv) red[(wu * 2 + wv) * 64 + bv * 32 + lane] = dg[bv];
+            for (int bv = 0; bv < 4; ++bv) red[(wu * 2 + wv) * 128 + bv * 32 + lane] = dg[bv];
         }
         __syncthreads();
         if (wu == 0 && fk == 0) {
 #pragma unroll
-            for (int bv = 0; bv < 2; ++bv) {
-                const int p = v0 + wv * 64 + bv * 32 + lane;
+            for (int bv = 0; bv < 4; ++bv) {
+                const int p = v0 + wv * 128 + bv * 32 + lane;
                 g.dgp[static_cast<int64_t>(ut) * g.P + p] =
-                    red[(0 * 2 + wv) * 64 + bv * 32 + lane] + red[(1 * 2 + wv) * 64 + bv * 32 + lane];
+                    red[(0 * 2 + wv) * 128 + bv * 32 + lane] + red[(1 * 2 + wv) * 128 + bv * 32 + lane];
             }
         }
     }

@@ -105,7 +105,7 @@ hipError_t launch_down_fp8(const Shape& s, const void* h, const int32_t* counts,
 hipError_t launch_quantize_fp8(int64_t rows, int cols, const void* w, uint8_t* q, float* scale, hipStream_t st);
 
 // Backward pass (bf16).  Workspace pieces, carved by backward_workspace_bytes
-// (base == nullptr only sizes it).  Rows are padded to 128 per expert.
+// (base == nullptr only sizes it).  Rows are padded to 256 per expert.
 struct BackwardWs {
     int32_t* idx;
     float* gate;
