@@ -280,6 +280,11 @@ struct GemmArgs {
     bf16_t* hg;             // [P, F]
     float* dgp;             // [U / kTU, P] partial dg sums
     int P;
+    // TOKEN_V with row-contiguous X: ksplit 2 cuts K at xsplit (X = xa for the
+    // first part, xb for the second) and writes the second part's sums
+    // c_split_stride elements after c0
+    int ksplit;
+    int64_t c_split_stride;
 };
 
 template <bool XRC, bool YRC, int EPI, bool TOKEN_V>
@@ -297,15 +302,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nut = g.U / kTU;
 
     // ---- tile of this block: (expert e, u tile ut, v tile vt), XCD-aware
-    int e = 0, ut = 0, vt = 0, kbeg = 0, klen = g.K;
+    int e = 0, ut = 0, vt = 0, kbeg = 0, klen = g.K, ksp = 0;
     if (TOKEN_V) {
         // v runs over the expert's rows: expert e owns nut * (len_e / kTV) tiles
         int total = 0;
         for (int j = 0; j < g.n_exp; ++j) total += (g.offsets[j + 1] - g.offsets[j]) / kTV * nut;
-        const int run = (total + 7) >> 3;
+        const int tiles = total * g.ksplit;
+        const int run = (tiles + 7) >> 3;
         if (static_cast<int>(blockIdx.x >> 3) >= run) return;
         int L = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
-        if (L >= total) return;
+        if (L >= tiles) return;
+        ksp = L / total;
+        L -= ksp * total;
         for (e = 0; e < g.n_exp; ++e) {
             const int nv = (g.offsets[e + 1] - g.offsets[e]) / kTV;
             if (L < nv * nut) {
@@ -332,6 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         klen = g.offsets[e + 1] - kbeg;
     }
     const int u0 = ut * kTU, v0 = vt * kTV;
+    if (TOKEN_V && g.ksplit > 1) klen = g.K / g.ksplit;
     const int ns = klen / kBK;
 
     // ---- operands
@@ -347,18 +356,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         ox.res[0] = ox.res[1] = bwd_rsrc(base);
         ox.split = 1 << 30;
     } else if (TOKEN_V) {
-        // X = weights [e][k][u] (k = d or F rows), second half for k >= xsplit
-        ox.res[0] = bwd_rsrc(g.xa + e * g.x_estride + u0);
-        ox.res[1] = bwd_rsrc((g.xsplit > 0 ? g.xb : g.xa) + e * g.x_estride + u0);
-        ox.split = g.xsplit > 0 ? g.xsplit / kBK : (1 << 30);
+        // X = weights [e][k][u] (k = d or F rows), second half for k >= xsplit;
+        // with the K split each part reads one half
+        if (g.ksplit > 1) {
+            ox.res[0] = ox.res[1] = bwd_rsrc((ksp ? g.xb : g.xa) + e * g.x_estride + u0);
+            ox.split = 1 << 30;
+        } else {
+            ox.res[0] = bwd_rsrc(g.xa + e * g.x_estride + u0);
+            ox.res[1] = bwd_rsrc((g.xsplit > 0 ? g.xb : g.xa) + e * g.x_estride + u0);
+            ox.split = g.xsplit > 0 ? g.xsplit / kBK : (1 << 30);
+        }
     } else {
         // X = per-row data [p][u], k = the expert's rows
         ox.res[0] = ox.res[1] = bwd_rsrc(g.xa + static_cast<int64_t>(kbeg) * g.ldx + u0);
         ox.split = 1 << 30;
     }
     if (!YRC) {
-        // Y rows v = permuted rows [p][k]
-        oy.res[0] = oy.res[1] = bwd_rsrc(g.y + static_cast<int64_t>(v0) * g.ldy);
+        // Y rows v = permuted rows [p][k], from this part's first k
+        oy.res[0] = oy.res[1] = bwd_rsrc(g.y + static_cast<int64_t>(v0) * g.ldy + ksp * klen);
     } else {
         // Y = per-row data [p][v], k = the expert's rows
         oy.res[0] = oy.res[1] = bwd_rsrc(g.y + static_cast<int64_t>(kbeg) * g.ldy + v0);
@@ -420,7 +435,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const int u = u0 + wu * 128 + bu * 32 + 8 * q4 + 4 * fk;
                     const f32x16_t& c = acc[bu][bv];
                     const f32x4_t o = {c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
-                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.c0) + static_cast<int64_t>(v) * g.ldc + u) = o;
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.c0) + ksp * g.c_split_stride +
+                                                static_cast<int64_t>(v) * g.ldc + u) = o;
                 }
         }
     } else if (EPI == kEpiDw) {
@@ -568,8 +584,10 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(const int32_t* __restri
         if (s < K) row[idx[t * K + s]] = gs[s] * (dg[s] - S);
 }
 
-// dx[t] = sum_s dxp[row_of[t, s]] (slot order) + sum_s dl[t, e_s] W_g[:, e_s], one rounding to bf16.
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ row_of,
+// dx[t] = sum_s (dxp + dxp_hi)[row_of[t, s]] (slot order) + sum_s dl[t, e_s] W_g[:, e_s], one
+// rounding to bf16; dxp and dxp_hi are the w1 and w3 parts of the per-row input gradients.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const float* __restrict__ dxp_hi,
+                                                     const int32_t* __restrict__ row_of,
                                                      const int32_t* __restrict__ idx, const float* __restrict__ dl,
                                                      const float* __restrict__ wg, int d, int n, int K,
                                                      bf16_t* __restrict__ dx) {
@@ -587,7 +605,9 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s) {
             if (s < K && p[s] >= 0) {
-                const float4 a = reinterpret_cast<const float4*>(dxp + static_cast<int64_t>(p[s]) * d)[c];
+                float4 a = reinterpret_cast<const float4*>(dxp + static_cast<int64_t>(p[s]) * d)[c];
+                const float4 b = reinterpret_cast<const float4*>(dxp_hi + static_cast<int64_t>(p[s]) * d)[c];
+                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;  // the w1 and w3 parts
                 v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
             }
         }
@@ -680,7 +700,7 @@ size_t backward_workspace_bytes(const Shape& s, BackwardWs* w, char* base) {
     v.da = reinterpret_cast<bf16_t*>(take(P * 2 * s.F * 2));
     v.hg = reinterpret_cast<bf16_t*>(take(P * s.F * 2));
     v.dgp = reinterpret_cast<float*>(take(nut * P * 4));
-    v.dxp = reinterpret_cast<float*>(take(P * s.d * 4));
+    v.dxp = reinterpret_cast<float*>(take(2 * P * s.d * 4));  // the w1 part, then the w3 part
     v.dl = reinterpret_cast<float*>(take(static_cast<size_t>(s.T) * s.n * 4));
     v.dwg_part = reinterpret_cast<float*>(take(chunks * s.d * s.n * 4));
     v.P = static_cast<int>(P);
@@ -730,7 +750,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.xa = w1b; g.xb = w3b; g.x_estride = static_cast<int64_t>(F) * d; g.ldx = d; g.xsplit = F;
     g.y = w.xp; g.ldy = d;
     g.U = 2 * F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;
-    g.c0 = w.a; g.ldc = 2 * F; g.P = P;
+    g.c0 = w.a; g.ldc = 2 * F; g.P = P; g.ksplit = 1;
     if ((err = launch_gemm<false, false, kEpiPreact, true>(g, grid8(static_cast<long long>(2 * F / kTU) * vmax), st)) !=
         hipSuccess)
         return err;
@@ -741,7 +761,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.y = w.dyp; g.ldy = d;
     g.U = F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = w.da; g.ldc = 2 * F;
-    g.a = w.a; g.gp = w.gp; g.hg = w.hg; g.dgp = w.dgp; g.P = P;
+    g.a = w.a; g.gp = w.gp; g.hg = w.hg; g.dgp = w.dgp; g.P = P; g.ksplit = 1;
     if ((err = launch_gemm<true, false, kEpiGrad, true>(g, grid8(static_cast<long long>(F / kTU) * vmax), st)) !=
         hipSuccess)
         return err;
@@ -752,8 +772,9 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.y = w.da; g.ldy = 2 * F;
     g.U = d; g.V = 0; g.K = 2 * F; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = w.dxp; g.ldc = d; g.P = P;
-    if ((err = launch_gemm<true, false, kEpiDx, true>(g, grid8(static_cast<long long>(d / kTU) * vmax), st)) !=
-        hipSuccess)
+    g.ksplit = 2;  // K = 2F cut at F: the w1 part and the w3 part, two partial buffers
+    g.c_split_stride = static_cast<int64_t>(P) * d;
+    if ((err = launch_gemm<true, false, kEpiDx, true>(g, grid8(2LL * (d / kTU) * vmax), st)) != hipSuccess)
         return err;
 
     // 4. dw2[e][j][f] = sum_p hg[p][f] dyp[p][j]: u = f, v = j
@@ -762,6 +783,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.y = w.dyp; g.ldy = d;
     g.U = F; g.V = d; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = dw2; g.c1 = dw2; g.c_estride = static_cast<int64_t>(d) * F; g.ldc = F; g.csplit = 0; g.P = P;
+    g.ksplit = 1;
     if ((err = launch_gemm<true, true, kEpiDw, false>(
              g, grid8(static_cast<long long>(n) * (F / kTU) * (d / kTV)), st)) != hipSuccess)
         return err;
@@ -772,6 +794,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.y = w.da; g.ldy = 2 * F;
     g.U = d; g.V = 2 * F; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = dw1; g.c1 = dw3; g.c_estride = static_cast<int64_t>(F) * d; g.ldc = d; g.csplit = F; g.P = P;
+    g.ksplit = 1;
     if ((err = launch_gemm<true, true, kEpiDw, false>(
              g, grid8(static_cast<long long>(n) * (d / kTU) * (2 * F / kTV)), st)) != hipSuccess)
         return err;
@@ -779,7 +802,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     // router gradient, dx, dW_g
     bwd_router_kernel<<<(T + 255) / 256, 256, 0, st>>>(w.idx, w.gate, w.row_of, w.dgp, F / kTU, P, T, n, K, w.dl);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    bwd_dx_kernel<<<T, 256, 0, st>>>(w.dxp, w.row_of, w.idx, w.dl, wg, d, n, K, static_cast<bf16_t*>(dx));
+    bwd_dx_kernel<<<T, 256, 0, st>>>(w.dxp, w.dxp + static_cast<int64_t>(P) * d, w.row_of, w.idx, w.dl, wg, d, n, K, static_cast<bf16_t*>(dx));
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int chunks = (T + kDwgTokens - 1) / kDwgTokens;
     bwd_dwg_partial_kernel<<<dim3((d + 255) / 256, chunks), 256, 0, st>>>(xb, w.dl, T, d, n, w.dwg_part);
