@@ -16,8 +16,9 @@
 //
 // The pass recomputes the routing and the gate/up pre-activations a1, a3
 // (nothing of the forward pass is kept), then runs five grouped GEMMs through
-// one MFMA kernel, over the expert-grouped rows padded to 256:
-//   1. a = [a1 | a3] = xp . [w1; w3]^T       u = 2F features, v = rows, K = d (fp32)
+// MFMA kernels, over the expert-grouped rows padded to 256 (the first product
+// reuses the forward pass's tiled gate/up kernel, the others share one kernel):
+//   1. a = [a1 | a3] = xp . [w1; w3]^T       K = d, fp32 (the forward gate/up tiled kernel)
 //   2. G = dyp . w2                           u = F, v = rows, K = d; epilogue
 //      forms h, dg partial sums, da = [da1 | da3] and hg = g h
 //   3. dxp = da . [w1; w3]                    u = d, v = rows, K = 2F
@@ -252,7 +253,7 @@ __device__ __forceinline__ void k_stage(const Operand& ox, const Operand& oy, co
     if (NEXT) sched_stage<kRead>();
 }
 
-enum Epi { kEpiPreact = 0, kEpiGrad = 1, kEpiDx = 2, kEpiDw = 3 };
+enum Epi { kEpiGrad = 1, kEpiDx = 2, kEpiDw = 3 };
 
 struct GemmArgs {
     // X (u operand): tile origin = x0 + (u0 or k0 rows) ...; see the tile set-up
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- epilogue.  32x32 C layout: lane l holds column v = l%32 of each
     // block and rows u = 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
     const int fk = lane >> 5;
-    if (EPI == kEpiPreact || EPI == kEpiDx) {
+    if (EPI == kEpiDx) {
 #pragma unroll
         for (int bv = 0; bv < 4; ++bv) {
             const int v = v0 + wv * 128 + bv * 32 + (lane & 31);
@@ -712,7 +713,7 @@ bool backward_fits(const Shape& s) {
     // 32-bit offsets: the per-row buffers (the largest, a: P x 2F fp32) and
     // the weights of one expert must stay below 2 GiB
     const long long P = static_cast<long long>(s.T) * s.K + static_cast<long long>(s.n) * (kTV - 1);
-    return P * 2LL * s.F * 4 < (1LL << 31) && 2LL * s.F * s.d * 2 < (1LL << 31) && s.F % kTU == 0 &&
+    return tiled_fits(s) && P * 2LL * s.F * 4 < (1LL << 31) && 2LL * s.F * s.d * 2 < (1LL << 31) && s.F % kTU == 0 &&
            s.d % kTU == 0;
 }
 
@@ -745,18 +746,12 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     const int vmax = (P + kTV - 1) / kTV;  // worst-case row tiles
     auto grid8 = [](long long tiles) { return static_cast<int>((tiles + 7) / 8 * 8); };
 
-    // 1. a = [a1 | a3]: X = [w1; w3] rows (k-contiguous), Y = xp rows
-    GemmArgs g{};
-    g.xa = w1b; g.xb = w3b; g.x_estride = static_cast<int64_t>(F) * d; g.ldx = d; g.xsplit = F;
-    g.y = w.xp; g.ldy = d;
-    g.U = 2 * F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;
-    g.c0 = w.a; g.ldc = 2 * F; g.P = P; g.ksplit = 1;
-    if ((err = launch_gemm<false, false, kEpiPreact, true>(g, grid8(static_cast<long long>(2 * F / kTU) * vmax), st)) !=
-        hipSuccess)
-        return err;
+    // 1. a = [a1 | a3] in fp32: the forward pass's tiled gate/up kernel with a
+    //    pre-activation epilogue (same rows, same tile order)
+    if ((err = launch_tiled_preact(s, x, w.row_src, w.counts, w.offsets, w1, w3, w.a, st)) != hipSuccess) return err;
 
+    GemmArgs g{};
     // 2. G = dyp . w2 with the gradient epilogue: X = w2[e] as [k = d][u = F]
-    g = GemmArgs{};
     g.xa = w2b; g.xb = w2b; g.x_estride = static_cast<int64_t>(d) * F; g.ldx = F; g.xsplit = 0;
     g.y = w.dyp; g.ldy = d;
     g.U = F; g.V = 0; g.K = d; g.offsets = w.offsets; g.n_exp = n;

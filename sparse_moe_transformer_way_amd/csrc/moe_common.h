@@ -145,6 +145,11 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
                         void* out, hipStream_t st, int ksplit = 1);
 
+// The gate/up tiled kernel storing the pre-activations a1 = w1 . x, a3 = w3 . x
+// in fp32 (a [P, 2F], padding rows zero) for the backward pass.
+hipError_t launch_tiled_preact(const Shape& s, const void* x, const int32_t* row_src, const int32_t* counts,
+                               const int32_t* offsets, const void* w1, const void* w3, float* a, hipStream_t st);
+
 // y_perm_hi (optional): second partial sum of the down projection, added to y_perm.
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
                           const float* gate, const void* residual, void* y, hipStream_t st,

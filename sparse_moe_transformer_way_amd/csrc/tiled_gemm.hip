@@ -212,7 +212,10 @@ __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1
     block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, f0, f1, acc);
 }
 
-template <bool DUAL>
+// PREACT (with DUAL): store the pre-activations a1 = w1 . x and a3 = w3 . x
+// in fp32 (out [P, 2 Nw]: a1 in columns 0..Nw-1, a3 after) instead of h, for
+// the backward pass.
+template <bool DUAL, bool PREACT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_kernel(
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int L = L_all - split * per_split;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
-    out = static_cast<char*>(out) + split * split_stride * (DUAL ? sizeof(bf16_t) : sizeof(float));
+    out = static_cast<char*>(out) + split * split_stride * (DUAL && !PREACT ? sizeof(bf16_t) : sizeof(float));
     // expert e owns tiles [sum of earlier experts' n_tt_e * n_wt, + n_tt_e * n_wt)
     int e = 0, ntt_e = 0;
     for (; e < n_exp; ++e) {
@@ -344,7 +347,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int p = p0 + rt;
         if (p >= row_end) continue;
         const bool real = rt < valid;
-        if (DUAL) {
+        if (DUAL && PREACT) {
+            float* arow = static_cast<float*>(out) + static_cast<size_t>(p) * ld_out;
+            const int fb = wt * (kTW / 2) + wave_w * 64;
+            const uint32_t keep = real ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4_t a1, a3;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        a1[u] = __uint_as_float(__float_as_uint(acc[jj][i][4 * q4 + u]) & keep);
+                        a3[u] = __uint_as_float(__float_as_uint(acc[jj + 2][i][4 * q4 + u]) & keep);
+                    }
+                    const int f = fb + jj * 32 + 8 * q4 + 4 * fk;
+                    *reinterpret_cast<f32x4_t*>(arow + f) = a1;
+                    *reinterpret_cast<f32x4_t*>(arow + Nw + f) = a3;
+                }
+        } else if (DUAL) {
             bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
             const int fb = wt * (kTW / 2) + wave_w * 64;
             // padding rows are written as zeros; a bit mask (not a branch or
@@ -415,6 +436,19 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
                                                n_wt, s.d, s.T * s.K, P, ksplit, split_stride, s.n, s.K);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled_preact(const Shape& s, const void* x, const int32_t* row_src, const int32_t* counts,
+                               const int32_t* offsets, const void* w1, const void* w3, float* a, hipStream_t st) {
+    if (!tiled_fits(s)) return hipErrorInvalidValue;
+    const int P = s.T * s.K + s.n * (kTT - 1);
+    const int n_tt = (P + kTT - 1) / kTT;
+    const int n_wt = s.F / (kTW / 2);
+    const int G = (n_tt * n_wt + 7) / 8 * 8;
+    tiled_kernel<true, true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts, offsets,
+                                                static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3), a,
+                                                s.d, s.F, s.d, n_wt, 2 * s.F, s.T * s.K, P, 1, 0, s.n, s.K);
     return hipGetLastError();
 }
 
