@@ -270,9 +270,9 @@ moe_status_t moe_layer_forward_fp8(const moe_layer_desc_t* desc, int32_t T, cons
  * fp32 accumulation; the pre-activations stay fp32, their gradients and g*h
  * are rounded once to bf16 (the operands of the next products); every
  * reduction over tokens runs in fp32 in a fixed order (deterministic).
- * T == 0 writes zero weight gradients.  Supported: bf16 layers whose per-row
- * buffers stay below 2 GiB (T * K + 127 n rows of 2F fp32); else
- * MOE_ERR_UNSUPPORTED.
+ * T == 0 writes zero weight gradients.  Supported: bf16 layers with
+ * (T * K + 255) * 2F * 2 bytes below 4 GiB (the longest 32-bit addressed span:
+ * one expert's rows of the pre-activation gradients); else MOE_ERR_UNSUPPORTED.
  * workspace: at least moe_backward_workspace_size(desc, T) bytes, 256-byte
  * aligned (0 = unsupported descriptor).
  */

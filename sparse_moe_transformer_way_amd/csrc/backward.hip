@@ -710,11 +710,14 @@ size_t backward_workspace_bytes(const Shape& s, BackwardWs* w, char* base) {
 }
 
 bool backward_fits(const Shape& s) {
-    // 32-bit offsets: the per-row buffers (the largest, a: P x 2F fp32) and
-    // the weights of one expert must stay below 2 GiB
-    const long long P = static_cast<long long>(s.T) * s.K + static_cast<long long>(s.n) * (kTV - 1);
-    return tiled_fits(s) && P * 2LL * s.F * 4 < (1LL << 31) && 2LL * s.F * s.d * 2 < (1LL << 31) && s.F % kTU == 0 &&
-           s.d % kTU == 0;
+    // Buffer resources are based at each tile's (or expert's) origin and
+    // offset in 32 bits: the longest such span is one expert's rows of da
+    // (at most T*K + 255 rows of 2F bf16), or one expert's weights.  The fp32
+    // pre-activations and every other per-row buffer are addressed through
+    // 64-bit pointers.
+    const long long rows = static_cast<long long>(s.T) * s.K + (kTV - 1);
+    return tiled_fits(s) && rows * 2LL * s.F * 2 < (1LL << 32) && 2LL * s.F * s.d * 2 < (1LL << 32) &&
+           s.F % kTU == 0 && s.d % kTU == 0;
 }
 
 hipError_t launch_zero_grads(const Shape& s, float* dwg, float* dw1, float* dw3, float* dw2, hipStream_t st) {

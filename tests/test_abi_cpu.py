@@ -189,7 +189,8 @@ def test_backward_descriptor_rules():
     assert moe.moe_backward_workspace_size(D(act_dtype=0, weight_dtype=0, d_model=512, d_ffn=512), 64) == 0
     assert moe.moe_backward_workspace_size(D(weight_dtype=2), 64) == 0
     assert moe.moe_backward_workspace_size(D(), -1) == 0
-    assert moe.moe_backward_workspace_size(D(), 1 << 20) == 0   # per-row buffers past 2 GiB
+    assert moe.moe_backward_workspace_size(D(), 16384) > 0       # the skewed prefill size
+    assert moe.moe_backward_workspace_size(D(), 80000) == 0     # one expert's rows of da past 4 GiB
     lib = _lib.lib
     f32 = ctypes.byref(D(act_dtype=0, weight_dtype=0, d_model=512, d_ffn=512))
     args = [FAKE] * 11
