@@ -206,17 +206,44 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const void* __restrict__ wa, const void* __restrict__ wb, const float* __restrict__ sa,
     const float* __restrict__ sb, void* __restrict__ out,
-    int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P, int topk) {
+    int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P, int topk, int tail_rows,
+    float* __restrict__ out_hi, int tail_parts) {
     // Two stage buffers (each 4 wave slices of 8 KB); after the K loop they
     // hold the cross-wave reduction [wave][token block][weight block][lane].
     __shared__ uint4 sb0[4 * kStreamWaveVec];
     __shared__ uint4 sb1[4 * kStreamWaveVec];
 
     const int e = blockIdx.y;
-    const int seg = offsets[e];
+    int seg = offsets[e];
     // rows [seg, seg_end) may be read and written: the segment, clamped to the buffers
     const int seg_end = min(offsets[e + 1], P);
-    const int cnt = min(counts[e], seg_end - seg);
+    int cnt = min(counts[e], seg_end - seg);
+    if (tail_rows > 0) {
+        // Tile-256 layout: only an expert's short tail past its full tiles (the
+        // tiled kernels skip that tile).  Rows of the tail's tile past the
+        // 16-row blocks written below are zeroed here: h padding (gate/up), or
+        // this pass's rows of the tiled kernel's second K-partial (down), which
+        // the combine adds.
+        const int r = cnt % kTiledRows;
+        if (r == 0 || r > tail_rows) return;
+        // the same decision as the tiled kernel's: gridDim.x is Nw / 64 here, the
+        // tiled kernel's weight tiles of 256 rows are Nw / 256, times its K parts
+        if (!tail_split_pays(offsets, counts, gridDim.y, Nw / kTiledRows * tail_parts)) return;
+        seg += cnt - r;
+        cnt = r;
+        if (DUAL) {
+            bf16_t* h = static_cast<bf16_t*>(out);
+            const int z0 = seg + ((r + 15) & ~15);
+            const int nz = max(0, seg_end - z0);
+            for (int i = threadIdx.x; i < nz * 4; i += 256)
+                *reinterpret_cast<uint4*>(h + static_cast<size_t>(z0 + (i >> 2)) * Nw + blockIdx.x * 32 +
+                                          (i & 3) * 8) = make_uint4(0, 0, 0, 0);
+        } else if (out_hi != nullptr) {
+            for (int i = threadIdx.x; i < r * 16; i += 256)
+                *reinterpret_cast<uint4*>(out_hi + static_cast<size_t>(seg + (i >> 4)) * Nw + blockIdx.x * 64 +
+                                          (i & 15) * 4) = make_uint4(0, 0, 0, 0);
+        }
+    }
     if (cnt <= 0) return;
     const int ntb = (cnt + 15) >> 4;
 
@@ -463,8 +490,10 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
         dim3 grid(s.F / 32, s.n);
         stream_kernel<true, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts,
                                                          offsets, w1, w3, nullptr, nullptr, h, s.d, s.F, s.d,
-                                                         s.T * s.K, pmax_rows(s, 16), s.K);
+                                                         s.T * s.K, pmax_rows(s, 16), s.K, 0, nullptr, 1);
     } else {
+        // (a short tail costs gate/up less than a full tile: its idle waves skip
+        // their reads and MFMAs, so streaming the tail does not pay here)
         return launch_tiled(s, true, x, row_src, counts, offsets, w1, w3, h, st);
     }
     return hipGetLastError();
@@ -485,7 +514,7 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
         stream_kernel<false, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts,
                                                           offsets, w2, nullptr, nullptr, nullptr,
                                                           y_perm, s.F, s.d, s.F, s.T * s.K,
-                                                          pmax_rows(s, 16), s.K);
+                                                          pmax_rows(s, 16), s.K, 0, nullptr, 1);
     } else {
         int ks = 1;
         if (y_perm_hi != nullptr) {
@@ -495,7 +524,13 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
             if (ks == 2 && y_perm_hi != y_perm + P * s.d) ks = 1;
         }
         if (n_parts != nullptr) *n_parts = ks;
-        return launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks);
+        hipError_t err = launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks, kTailRows);
+        if (err != hipSuccess) return err;
+        dim3 grid(s.d / 64, s.n);
+        stream_kernel<false, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts, offsets,
+                                                          w2, nullptr, nullptr, nullptr, y_perm, s.F, s.d, s.F,
+                                                          s.T * s.K, pmax_rows(s, 256), s.K, kTailRows,
+                                                          ks == 2 ? y_perm_hi : nullptr, ks);
     }
     return hipGetLastError();
 }
@@ -506,7 +541,7 @@ hipError_t launch_gate_up_fp8(const Shape& s, const void* x, const int32_t* row_
     dim3 grid(s.F / 32, s.n);
     stream_kernel<true, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts, offsets, w1,
                                                     w3, s1, s3, h, s.d, s.F, s.d, s.T * s.K, pmax_rows(s, 16),
-                                                    s.K);
+                                                    s.K, 0, nullptr, 1);
     return hipGetLastError();
 }
 
@@ -515,7 +550,7 @@ hipError_t launch_down_fp8(const Shape& s, const void* h, const int32_t* counts,
     dim3 grid(s.d / 64, s.n);
     stream_kernel<false, true><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts, offsets, w2,
                                                      nullptr, s2, nullptr, y_perm, s.F, s.d, s.F, s.T * s.K,
-                                                     pmax_rows(s, 16), s.K);
+                                                     pmax_rows(s, 16), s.K, 0, nullptr, 1);
     return hipGetLastError();
 }
 

@@ -68,6 +68,32 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 // hipGetLastError() status of its launches.  Shapes are validated by the ABI.
 // ---------------------------------------------------------------------------
 // Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
+// Token rows of a tile of the LDS-tiled MFMA kernels, and the largest
+// remainder of an expert's rows (past its full tiles) that the weight-streaming
+// kernels take over from them in the tile-256 layout: such a tail would cost a
+// whole tile there, while streaming reads the expert's weights once.
+constexpr int kTiledRows = 256;
+constexpr int kTailRows = 64;
+constexpr int kComputeUnits = 256;  // MI355X: a round of tiled-kernel tiles
+
+// Whether moving the short tails out of the tiled kernel saves it a round of
+// tiles: ceil(tiles / CUs) drops.  Both the tiled kernel and the streaming
+// tail pass evaluate this from the same device-side counts, so they agree.
+// tiles_per_row_tile: tiles of one 256-row token tile (weight tiles x K parts).
+__device__ __forceinline__ bool tail_split_pays(const int32_t* offsets, const int32_t* counts, int n_exp,
+                                                int tiles_per_row_tile) {
+    int with_tail = 0, without = 0;
+    for (int e = 0; e < n_exp; ++e) {
+        const int len = offsets[e + 1] - offsets[e];
+        const int c = counts[e];
+        const int r = c % kTiledRows;
+        without += len / kTiledRows;
+        with_tail += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
+    }
+    const int per_round = kComputeUnits;
+    return (with_tail * tiles_per_row_tile + per_round - 1) / per_round <
+           (without * tiles_per_row_tile + per_round - 1) / per_round;
+}
 constexpr int kMaxExperts = 16;
 constexpr int kMaxTopK = 4;
 
@@ -141,9 +167,11 @@ int tiled_down_ksplit(const Shape& s);
 
 // LDS-tiled MFMA kernels (bf16, tile_m 256): gate_up selects SiLU(act.wa) * (act.wb)
 // into bf16 `out`, otherwise act.wa into fp32 `out`.
+// tail_rows > 0: an expert's last tile holding at most tail_rows real rows is
+// skipped (left to the weight-streaming kernels).
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
-                        void* out, hipStream_t st, int ksplit = 1);
+                        void* out, hipStream_t st, int ksplit = 1, int tail_rows = 0);
 
 // The gate/up tiled kernel storing the pre-activations a1 = w1 . x, a3 = w3 . x
 // in fp32 (a [P, 2F], padding rows zero) for the backward pass.

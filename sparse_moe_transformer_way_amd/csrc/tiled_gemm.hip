@@ -57,7 +57,7 @@ namespace moe {
 namespace {
 
 constexpr int kTW = 256;                     // weight rows per tile
-constexpr int kTT = 256;                     // token rows per tile
+constexpr int kTT = kTiledRows;              // token rows per tile
 constexpr int kBK = 64;                      // k per LDS buffer (one "block")
 constexpr int kChunks = kBK / 8;             // 16-byte chunks per LDS row (128-byte rows)
 constexpr int kBufVec = (kTW + kTT) * kChunks;  // uint4 per buffer (64 KB)
@@ -69,6 +69,15 @@ typedef void __attribute__((address_space(3)))* lptr_t;
 
 // g(r) = r1 | r2 << 1 | r4 << 2
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
+
+// Token tiles of an expert's segment (length len, padded to kTT, count rows).
+// With tail_rows > 0 a last tile holding at most tail_rows real rows is left
+// to the weight-streaming kernels (it would cost a whole tile here); the
+// kernel only does so when that saves a round of tiles (tail_split_pays).
+__device__ __forceinline__ int token_tiles(int len, int count, int tail_rows) {
+    const int r = count % kTT;
+    return (r > 0 && r <= tail_rows) ? count / kTT : len / kTT;
+}
 
 // Buffer resource over [base, base + 4 GiB); every offset the kernel adds is
 // in range by construction.
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_wt,
-    int ld_out, int n_src, int P, int ksplit, size_t split_stride, int n_exp, int topk) {
+    int ld_out, int n_src, int P, int ksplit, size_t split_stride, int n_exp, int topk, int tail_rows) {
     __shared__ uint4 b0[kBufVec];
     __shared__ uint4 b1[kBufVec];
 
@@ -229,8 +238,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // token tiles x n_wt per K part); the segments hold fewer.  Those tiles are dealt out
     // evenly: XCD x (workgroups b with b % 8 == x) takes a contiguous run of
     // ceil(total / 8) of them, and the remaining workgroups exit here.
+    if (tail_rows > 0 && !tail_split_pays(offsets, counts, n_exp, n_wt * ksplit)) tail_rows = 0;
     int per_split = 0;
-    for (int j = 0; j < n_exp; ++j) per_split += (offsets[j + 1] - offsets[j]) / kTT * n_wt;
+    for (int j = 0; j < n_exp; ++j) per_split += token_tiles(offsets[j + 1] - offsets[j], counts[j], tail_rows) * n_wt;
     const int total = per_split * ksplit;
     const int run = (total + 7) >> 3;
     if (static_cast<int>(blockIdx.x >> 3) >= run) return;
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // expert e owns tiles [sum of earlier experts' n_tt_e * n_wt, + n_tt_e * n_wt)
     int e = 0, ntt_e = 0;
     for (; e < n_exp; ++e) {
-        ntt_e = (offsets[e + 1] - offsets[e]) / kTT;  // segments are padded to kTT rows
+        ntt_e = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
         if (L < ntt_e * n_wt) break;
         L -= ntt_e * n_wt;
     }
@@ -420,7 +430,7 @@ int tiled_down_ksplit(const Shape& s) {
 
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
-                        void* out, hipStream_t st, int ksplit) {
+                        void* out, hipStream_t st, int ksplit, int tail_rows) {
     if (!tiled_fits(s)) return hipErrorInvalidValue;
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
@@ -431,11 +441,11 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
                                               static_cast<const bf16_t*>(wa), static_cast<const bf16_t*>(wb),
                                               out, s.d, s.F, s.d, n_wt, s.F, s.T * s.K, P,
-                                              ksplit, split_stride, s.n, s.K);
+                                              ksplit, split_stride, s.n, s.K, tail_rows);
     else
         tiled_kernel<false><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), nullptr, counts, offsets,
                                                static_cast<const bf16_t*>(wa), nullptr, out, s.F, s.d, s.F,
-                                               n_wt, s.d, s.T * s.K, P, ksplit, split_stride, s.n, s.K);
+                                               n_wt, s.d, s.T * s.K, P, ksplit, split_stride, s.n, s.K, tail_rows);
     return hipGetLastError();
 }
 
@@ -448,7 +458,7 @@ hipError_t launch_tiled_preact(const Shape& s, const void* x, const int32_t* row
     const int G = (n_tt * n_wt + 7) / 8 * 8;
     tiled_kernel<true, true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts, offsets,
                                                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3), a,
-                                                s.d, s.F, s.d, n_wt, 2 * s.F, s.T * s.K, P, 1, 0, s.n, s.K);
+                                                s.d, s.F, s.d, n_wt, 2 * s.F, s.T * s.K, P, 1, 0, s.n, s.K, 0);
     return hipGetLastError();
 }
 

@@ -133,8 +133,11 @@ def test_permute_ignores_out_of_range_experts():
 # Grouped expert projections
 # ---------------------------------------------------------------------------
 
+# tile 256 with T = 1150 and 2100 leaves most experts a remainder of at most
+# 64 rows past their full tiles (taken by the weight-streaming kernels)
 CASES = [("f32", 64, 128, 256, 16), ("f32", 5, 64, 40, 16), ("bf16", 40, 512, 1024, 16),
          ("bf16", 3, 1024, 512, 16), ("bf16", 1500, 512, 1024, 256), ("bf16", 150, 1024, 512, 256),
+         ("bf16", 1150, 512, 1024, 256), ("bf16", 2100, 1024, 512, 256),
          ("bf16", 200, 512, 512, 16), ("bf16", 600, 512, 512, 16)]
 
 

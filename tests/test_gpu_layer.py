@@ -53,6 +53,8 @@ def check_full(inp, tol):
     ("bf16", 65, 512, 1024),    # first T on the tiled kernels, few rows per expert
     ("bf16", 1000, 512, 1024),  # tiled kernels, ~250 rows per expert
     ("bf16", 2500, 1024, 512),
+    ("bf16", 1150, 512, 1024),  # short expert tails past full 256-row tiles
+    ("bf16", 2100, 1024, 512),
 ])
 def test_layer_small(dtype, T, d, F):
     init = "fanin" if dtype == "f32" else "mixtral"
