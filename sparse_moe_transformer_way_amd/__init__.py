@@ -95,7 +95,7 @@ def moe_block_workspace_size(desc: LayerDesc, T: int) -> int:
 
 
 def moe_router_topk(desc, x, w_gate, topk_idx=None, topk_gate=None, logits_out=None, stream=None):
-    """Router logits, Top-2 and gates.  Returns (topk_idx [T,K] int32, topk_gate [T,K] fp32)."""
+    """Router logits, Top-K and gates.  Returns (topk_idx [T,K] int32, topk_gate [T,K] fp32)."""
     T = x.shape[0]
     dev = x.device
     if topk_idx is None:

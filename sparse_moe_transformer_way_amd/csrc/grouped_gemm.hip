@@ -3,8 +3,9 @@
 // Expert i computes E_i(x) = w2_i . (SiLU(w1_i . x) * (w3_i . x)) (Mixtral of
 // Experts, paper-graph-ui page, section 3.4, "Expert Network Structure
 // (SwiGLU)", with w1 = gate, w3 = up, w2 = down).  Each expert sees only the
-// rows routed to it (dropless top-2, same section, routing paragraphs), packed
-// contiguously per expert and padded to the row tile.
+// rows routed to it (dropless top-K routing, K = 2 in Mixtral; same section,
+// routing paragraphs), packed contiguously per expert and padded to the row
+// tile.
 //
 // Both projections are "NT" contractions: out[row][j] = sum_k act[row][k] *
 // W[j][k] with k contiguous in both operands (W is [out_features, in_features]
