@@ -116,12 +116,60 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     for (int p = s_off[NE] + tid; p < P_max; p += kThreads) row_src[p] = -1;
 }
 
+// Up to 64 assignments (a decode step): one wave, lane a holds assignment a.
+// Expert e's members are the lanes of ballot(idx == e); a member's rank among
+// them (the popcount of the lower lanes) is its place in the segment, so the
+// order is the same ascending-assignment order as above, without a barrier.
+__global__ __launch_bounds__(64) void permute_wave_kernel(const int32_t* __restrict__ idx, int TK, int n,
+                                                          int tile_m, int P_max, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_src,
+                                                          int32_t* __restrict__ row_of) {
+    const int lane = threadIdx.x;
+    const int mine = lane < TK ? idx[lane] : -1;
+    const bool real = mine >= 0 && mine < n;
+    int seg_off[kMaxExperts + 1], seg_cnt[kMaxExperts];
+    int off = 0, pos = -1;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+        seg_off[e] = off;
+        seg_cnt[e] = 0;
+        if (e < n) {
+            const unsigned long long m = __ballot(real && mine == e);
+            const int c = __popcll(m);
+            seg_cnt[e] = c;
+            if (lane == 0) {
+                counts[e] = c;
+                offsets[e] = off;
+            }
+            if (real && mine == e) pos = off + __popcll(m & ((1ull << lane) - 1ull));
+            off += (c + tile_m - 1) / tile_m * tile_m;
+        }
+    }
+    seg_off[kMaxExperts] = off;
+    if (lane == 0) offsets[n] = off;
+    if (lane < TK) row_of[lane] = pos;
+    if (pos >= 0) row_src[pos] = lane;
+    // every other row is padding: inside a segment past its count, or past the last segment
+    for (int p = lane; p < P_max; p += 64) {
+        bool pad = p >= off;
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e)
+            if (e < n && p >= seg_off[e] + seg_cnt[e] && p < seg_off[e + 1]) pad = true;
+        if (pad) row_src[p] = -1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* row_src, int32_t* row_of, hipStream_t st) {
     const int TK = s.T * s.K;
     const int P_max = TK + s.n * (tile_m - 1);
+    if (TK <= 64) {
+        permute_wave_kernel<<<1, 64, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
+        return hipGetLastError();
+    }
     if (s.n <= 8)
         permute_kernel<8><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
     else

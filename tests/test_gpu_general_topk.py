@@ -78,7 +78,8 @@ def _random_idx(T, n, K, seed):
     return np.stack([rng.permutation(n)[:K] for _ in range(T)]).astype(np.int32).reshape(T, K)
 
 
-@pytest.mark.parametrize("n,K,T,tile_m", [(16, 4, 1000, 256), (16, 4, 37, 16), (3, 1, 500, 16),
+@pytest.mark.parametrize("n,K,T,tile_m", [(16, 4, 1000, 256), (16, 4, 37, 16), (16, 4, 16, 16),
+                                          (13, 3, 21, 16), (3, 1, 64, 16), (3, 1, 500, 16),
                                           (5, 3, 2000, 256), (12, 4, 16384, 256), (9, 2, 0, 16),
                                           (1, 1, 300, 256)])
 def test_permute_general(n, K, T, tile_m):

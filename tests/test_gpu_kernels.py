@@ -93,7 +93,9 @@ def _random_idx(T, seed, skew=False):
     return np.stack([rng.permutation(8)[:2] for _ in range(T)]).astype(np.int32).reshape(T, 2)
 
 
-@pytest.mark.parametrize("T,tile_m,skew", [(0, 16, False), (1, 16, False), (37, 16, False),
+@pytest.mark.parametrize("T,tile_m,skew", [(0, 16, False), (1, 16, False), (31, 16, False),
+                                           (32, 16, False), (32, 256, False), (32, 16, True),
+                                           (33, 16, False), (37, 16, False),
                                            (300, 256, False), (2000, 256, False),
                                            (5000, 16, False), (16384, 256, False),
                                            (999, 256, True), (64, 16, True)])
@@ -110,12 +112,12 @@ def test_permute(T, tile_m, skew):
     np.testing.assert_array_equal(row_of.cpu().numpy(), ref["row_of"])
 
 
-def test_permute_ignores_out_of_range_experts():
-    T = 100
+@pytest.mark.parametrize("T", [100, 20])
+def test_permute_ignores_out_of_range_experts(T):
     idx = _random_idx(T, 5)
     idx[3, 1] = -1
-    idx[50, 0] = 8
-    idx[99, 1] = 1 << 20
+    idx[T // 2, 0] = 8
+    idx[T - 1, 1] = 1 << 20
     counts, offsets, row_src, row_of = moe.moe_permute(moe.make_desc(4096, 14336),
                                                        torch.from_numpy(idx).cuda(), 16)
     flat = idx.ravel()
