@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer tokens/s on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny|decode_fp8|backward]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|tiny|stack|decode_fp8|backward]
 
 One step is one pass of the whole layer (router -> permute -> gate/up + SwiGLU ->
 down -> combine) over one batch of synthetic tokens already resident in HBM.
@@ -14,6 +14,9 @@ decode_fp8 is the decode workload with its expert weights quantized to FP8
 (E4M3, one scale per row) on the device before any timing.  backward times
 moe_layer_backward (all gradients of the layer) on the prefill workload's
 inputs with a seeded upstream gradient; its roofline covers the whole pass.
+stack runs 32 pre-norm MoE blocks (h <- h + MoE(RMSNorm(h)), independent
+weights per layer, ~90 GB resident) over 8192 tokens: one step is the whole
+stack, and the roofline is that of the gate/up kernel averaged over the layers.
 
 Prints one JSON line.  Only one GPU is used; --gpus above 1 is refused.
 """
@@ -31,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X + % of HBM (decode) / MFMA (prefill) roofline"
-WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3, "decode_fp8": 1, "backward": 2}
+WORKLOADS = {"tiny": 0, "decode": 1, "prefill": 2, "skewed": 3, "stack": 4, "decode_fp8": 1, "backward": 2}
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
@@ -174,6 +177,92 @@ def bench_backward(args, inp, spec):
     print(json.dumps(out), flush=True)
 
 
+def bench_stack(args, spec):
+    """Steps of the 32-block stack between device synchronisations, then the
+    gate/up kernel of every layer between HIP events on the launch stream."""
+    import torch
+    import moe_inputs as mi
+    import sparse_moe_transformer_way_amd as moe
+
+    T, d, F, n, K, L = spec["T"], spec["d"], spec["F"], spec["n"], spec["K"], spec["layers"]
+    dev = torch.device("cuda")
+    layers = [mi.stack_layer_weights(l, d, F, n, seed=args.seed, device="cuda") for l in range(L)]
+    h0 = mi.stack_input(T, d, seed=args.seed).to(dev)
+    desc = moe.make_desc(d, F, n, K)
+    tile_m = moe.moe_default_tile_m(desc, T)
+    P = moe.moe_max_permuted_rows(desc, T, tile_m)
+    h = torch.empty_like(h0)
+    ws = torch.empty(moe.moe_block_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    cnt = torch.empty((L, n), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        # block 0 reads h0, the others update h in place
+        for l, (wg, w1, w3, w2) in enumerate(layers):
+            moe.moe_block_forward(desc, h0 if l == 0 else h, wg, w1, w3, w2, eps=1e-5, h_out=h,
+                                  topk_idx_out=idx, counts_out=cnt[l], workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # the gate/up kernel of each layer, on that layer's routing of the stack's
+    # last h states (normed input, router and permute run untimed first)
+    x = torch.empty_like(h0)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(P, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, K), dtype=torch.int32, device=dev)
+    hbuf = torch.empty((P, F), dtype=torch.bfloat16, device=dev)
+    reps = max(1, min(args.steps, 5))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L * reps)]
+    for r in range(reps):
+        for l, (wg, w1, w3, w2) in enumerate(layers):
+            moe.moe_rmsnorm(h, 1e-5, x_out=x, stream=stream)
+            moe.moe_router_topk(desc, x, wg, idx, gate, stream=stream)
+            moe.moe_permute(desc, idx, tile_m, counts, offsets, row_src, row_of, stream=stream)
+            ev[r * L + l][0].record(stream)
+            moe.moe_expert_gate_up(desc, T, tile_m, x, row_src, counts, offsets, w1, w3, hbuf, stream=stream)
+            ev[r * L + l][1].record(stream)
+    torch.cuda.synchronize()
+    gu_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    TK = T * K
+    gu_flops = 4.0 * TK * d * F
+    achieved = gu_flops / (gu_ms / 1e3) / 1e12
+    block_flops = 2.0 * TK * 3 * d * F + 2.0 * T * d * n
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec["name"], "T": T, "layers": L, "d_model": d, "d_ffn": F, "n_experts": n,
+                   "top_k": K, "tile_m": tile_m, "expert_counts_last_layer": cnt[L - 1].cpu().tolist()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gate_up_tiled (mean over the layers)", "kernel_ms": round(gu_ms, 4),
+                     "algorithmic_per_launch": gu_flops},
+        "stack": {"layer_tokens_per_s": round(T * L / (ms / 1e3), 1), "ms_per_layer": round(ms / L, 4),
+                  "mfma_frac": round(block_flops * L / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -191,6 +280,9 @@ def main():
 
     wl = WORKLOADS[args.workload]
     spec = mi.WORKLOADS[wl]
+    if args.workload == "stack":
+        bench_stack(args, spec)
+        return
     inp = mi.make_workload(wl, seed=args.seed)
     if args.workload == "backward":
         bench_backward(args, inp, spec)
