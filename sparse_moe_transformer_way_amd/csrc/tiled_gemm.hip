@@ -36,21 +36,22 @@
 //     0-7 with 16-23, 8-15 with 24-31, measured with SQ_LDS_BANK_CONFLICT);
 //     in each phase the 8 even rows and the 8 odd rows get 8 distinct chunks,
 //     so the phase covers all 64 banks.  The copies write whole 1 KB runs.
-//   * Tile order: workgroup b runs on XCD b % 8, and each XCD gets an equal
-//     contiguous run of an expert-major enumeration of the tiles the segments
-//     actually hold (computed on the device from the segment offsets; the grid
-//     is sized for the worst case and the spare workgroups exit): expert by expert, groups of G weight tiles x all of the
-//     expert's token tiles, G ~ 32 / (the expert's token tiles).  The ~32 tiles
-//     an XCD runs at once (32 CUs) then read the same few weight and token
-//     tiles, so each k-slice comes from HBM once and from its L2 after that.
-//     (Measured on MI355X: with every tile's data L2-resident the kernels ran
-//     16% (gate/up) and 35% (down) faster than with an order that let a round
-//     straddle two experts.)
+//   * Tile order (tile_contiguous, tile_by_column): workgroup b runs on XCD
+//     b % 8; the tiles the segments actually hold are enumerated on the device
+//     from the segment offsets (the grid is sized for the worst case and the
+//     spare workgroups exit), in groups of a few weight tiles x all of an
+//     expert's token tiles, so the tiles an XCD runs at once share their data
+//     in its L2.
+//   * An expert's last token tile with at most 128 real rows runs as a narrow
+//     tile (narrow_tile): 64 or 128 token rows, the weight rows split over the
+//     four waves.
 //   * Padding rows of a token tile copy a real row (gate/up) or the padded rows
 //     of h (down); their outputs are masked in the epilogue.
 //   * K may be cut into two parts (down projection with few tiles): part s
 //     covers k in [s*K/2, (s+1)*K/2) and writes its own fp32 output buffer.
 #include "moe_common.h"
+
+#include <utility>
 
 namespace moe {
 
@@ -221,6 +222,319 @@ __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1
     block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, f0, f1, acc);
 }
 
+// ---- Narrow tiles.  An expert's last token tile often holds few real rows
+// (its count just past a multiple of 256).  In the layout above the waves
+// with any real row still run their whole 128 x 128 block of MFMAs, so such a
+// tile costs about as much as a full one.  A narrow tile keeps the 256 weight
+// rows but takes TN = 32 * TB token rows (TB = 2 or 4), and the four waves
+// split the weight rows instead: wave w owns LDS weight rows 32w.. and
+// 128 + 32w.. (gate/up: the same 32 rows f of w1 and of w3) or 64w .. 64w + 63
+// (down), against all TN token rows: 2 x TB blocks of 32 x 32, a quarter or
+// half of a full tile's MFMAs.  The weight copies are the full tile's; each
+// wave copies TN / 4 token rows.
+// (A plain struct: the host pass of hipcc rejects a class template holding a
+// buffer resource when it is passed on to a templated device function.)
+struct NarrowCtx {
+    __amdgpu_buffer_rsrc_t tres;
+    uint32_t to[4];   // lane byte offsets of token copy group jj (TB of them)
+    int tstride;      // down: bytes between 8-row token groups; 0 for gate/up
+    int dmat;         // uint4 offset of this wave's first token copy group (token half)
+    int rd[4];        // per (half of the block, k16 half): fragment index of the lane's row in a block
+    int wb[2];        // uint4 offset of this wave's two weight blocks
+};
+
+template <bool DUAL, int TB>
+__device__ __forceinline__ void copy_narrow(const TileCtx& c, const NarrowCtx& n, uint4* __restrict__ buf,
+                                            int k0, int j) {
+    if (j < 8) {
+        copy_one<DUAL>(c, buf, k0, j);
+    } else {
+        const int jj = j - 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(n.tres, (lptr_t)(buf + kTW * kChunks + n.dmat + jj * kGroupVec),
+                                                 16, n.to[jj], DUAL ? 2 * k0 : jj * n.tstride + 2 * k0, 0, 0);
+    }
+}
+
+// Fragments of half s of the block: [k16 half h][2 weight blocks, TB token blocks]
+template <int TB>
+__device__ __forceinline__ void read_narrow(const NarrowCtx& n, const uint4* __restrict__ buf, int s,
+                                            u32x4_t (&f)[2 * (2 + TB)]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4* p = buf + n.rd[2 * s + h];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) f[h * (2 + TB) + b] = __builtin_bit_cast(u32x4_t, p[n.wb[b]]);
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+            f[h * (2 + TB) + 2 + i] = __builtin_bit_cast(u32x4_t, p[(kTW + 32 * i) * kChunks]);
+    }
+}
+
+template <int TB>
+__device__ __forceinline__ void mfma_narrow(const u32x4_t (&f)[2 * (2 + TB)], f32x16_t (&acc)[2][TB]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                acc[b][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(f[h * (2 + TB) + b]), as_bf16x8(f[h * (2 + TB) + 2 + i]), acc[b][i], 0, 0, 0);
+}
+
+// 4 * TB MFMAs, each followed by its share of the stage's fragment reads
+// (READ) and of the block's 8 + TB copies (COPY).
+template <int TB, bool READ, bool COPY, int U>
+__device__ __forceinline__ void sched_narrow_unit() {
+    constexpr int kM = 4 * TB;
+    constexpr int kR = (U + 1) * 2 * (2 + TB) / kM - U * 2 * (2 + TB) / kM;
+    constexpr int kC = (U + 1) * (8 + TB) / kM - U * (8 + TB) / kM;
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (READ && kR > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kR, 0);
+    if constexpr (COPY && kC > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kC, 0);
+}
+
+template <int TB, bool READ, bool COPY, int... U>
+__device__ __forceinline__ void sched_narrow_seq(std::integer_sequence<int, U...>) {
+    (sched_narrow_unit<TB, READ, COPY, U>(), ...);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TB, bool READ, bool COPY>
+__device__ __forceinline__ void sched_narrow() {
+    sched_narrow_seq<TB, READ, COPY>(std::make_integer_sequence<int, 4 * TB>{});
+}
+
+// block_step for a narrow tile (every wave is active).
+template <bool DUAL, int TB, bool COPY, bool NEXT>
+__device__ __forceinline__ void narrow_step(const TileCtx& c, const NarrowCtx& n, uint4* __restrict__ cur,
+                                            const uint4* __restrict__ nxt, int kb, u32x4_t (&f0)[2 * (2 + TB)],
+                                            u32x4_t (&f1)[2 * (2 + TB)], f32x16_t (&acc)[2][TB]) {
+    read_narrow<TB>(n, cur, 1, f1);
+    mfma_narrow<TB>(f0, acc);
+    sched_narrow<TB, true, false>();
+    if (NEXT) block_barrier<0>();
+    if (COPY) {
+#pragma unroll
+        for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, cur, (kb + 2) * kBK, j);
+    }
+    if (NEXT) read_narrow<TB>(n, nxt, 0, f0);
+    mfma_narrow<TB>(f1, acc);
+    sched_narrow<TB, NEXT, COPY>();
+}
+
+// The whole narrow tile: copies, K loop, epilogue.  Gate/up also writes zeros
+// to the segment's rows past the TN token rows (its padding rows), in the
+// tile's 128 columns of h.
+template <bool DUAL, int TB>
+__device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __restrict__ act,
+                                            const int32_t* __restrict__ row_src, void* __restrict__ out,
+                                            uint4* b0, uint4* b1, int kpart, int kbase, int ld_act, int ld_out,
+                                            int n_src, int topk, int wt, int p0, int valid, int row_end) {
+    constexpr int TN = 32 * TB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fr = lane & 31;
+    const int fk = lane >> 5;
+    const int rl = lane >> 3;
+
+    NarrowCtx n;
+    {
+        // token copy group jj of wave w fills token rows r = w * TN/4 + 8 jj + l/8;
+        // bit 4 of r (the only bit of g(r) above the row-in-group bits) is fixed per group
+        const int ch0 = (lane & 7) ^ swz(rl);
+        const int ch1 = (lane & 7) ^ swz(16 + rl);
+        const int r0 = wave * (TN / 4);
+        if (DUAL) {
+            n.tres = make_rsrc(act + kbase);
+            const int first_src = row_src[p0];
+#pragma unroll
+            for (int jj = 0; jj < TB; ++jj) {
+                const int r = r0 + 8 * jj + rl;
+                int src = (r < valid) ? row_src[p0 + r] : first_src;
+                if (src < 0 || src >= n_src) src = first_src;
+                if (src < 0 || src >= n_src) src = 0;
+                const int ch = (((r0 + 8 * jj) >> 4) & 1) ? ch1 : ch0;
+                n.to[jj] = static_cast<uint32_t>(
+                    (static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act + 8 * ch) * 2);
+            }
+            n.tstride = 0;
+        } else {
+            // rows p0 + r0 .. + TN/4 of h, inside the expert's padded segment
+            n.tres = make_rsrc(act + static_cast<size_t>(p0 + r0) * ld_act + kbase);
+#pragma unroll
+            for (int jj = 0; jj < TB; ++jj) {
+                const int ch = (((r0 + 8 * jj) >> 4) & 1) ? ch1 : ch0;
+                n.to[jj] = (static_cast<uint32_t>(rl) * ld_act + 8u * ch) * 2u;
+            }
+            n.tstride = 8 * ld_act * 2;
+        }
+        n.dmat = r0 * kChunks;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) n.rd[q] = fr * kChunks + ((2 * q + fk) ^ swz(fr));
+        n.wb[0] = (DUAL ? 32 * wave : 64 * wave) * kChunks;
+        n.wb[1] = (DUAL ? kTW / 2 + 32 * wave : 64 * wave + 32) * kChunks;
+    }
+
+    f32x16_t acc[2][TB];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[b][i][q] = 0.0f;
+
+    const int nb = kpart / kBK;  // a multiple of 4, >= 4
+#pragma unroll
+    for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b0, 0, j);
+#pragma unroll
+    for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b1, kBK, j);
+    block_barrier<8 + TB>();  // block 0 has landed
+    u32x4_t f0[2 * (2 + TB)], f1[2 * (2 + TB)];
+    read_narrow<TB>(n, b0, 0, f0);
+    int kb = 0;
+    do {
+        narrow_step<DUAL, TB, true, true>(c, n, b0, b1, kb, f0, f1, acc);
+        narrow_step<DUAL, TB, true, true>(c, n, b1, b0, kb + 1, f0, f1, acc);
+        kb += 2;
+    } while (kb < nb - 2);
+    narrow_step<DUAL, TB, false, true>(c, n, b0, b1, kb, f0, f1, acc);
+    narrow_step<DUAL, TB, false, false>(c, n, b1, b0, kb + 1, f0, f1, acc);
+
+    // epilogue (32x32 C layout as in the full tile)
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+        const int rt = 32 * i + fr;
+        const int p = p0 + rt;
+        if (p >= row_end) continue;
+        const bool real = rt < valid;
+        if (DUAL) {
+            bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
+            const int fb = wt * (kTW / 2) + 32 * wave;
+            const uint32_t keep = real ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float hv = silu_f32(acc[0][i][4 * q4 + u]) * acc[1][i][4 * q4 + u];
+                    v[u] = __uint_as_float(__float_as_uint(hv) & keep);
+                }
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(hrow + fb + 8 * q4 + 4 * fk) = o;
+            }
+        } else {
+            if (!real) continue;
+            float* yrow = static_cast<float*>(out) + static_cast<size_t>(p) * ld_out;
+            const int jb = wt * kTW + 64 * wave;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4_t v = {acc[b][i][4 * q4], acc[b][i][4 * q4 + 1], acc[b][i][4 * q4 + 2],
+                                 acc[b][i][4 * q4 + 3]};
+                    *reinterpret_cast<f32x4_t*>(yrow + jb + 32 * b + 8 * q4 + 4 * fk) = v;
+                }
+        }
+    }
+    if (DUAL) {
+        // padding rows p0 + TN .. of the segment: 128 columns of zeros (16 x 16 bytes) each
+        const int z0 = p0 + TN;
+        const int z1 = min(p0 + kTT, row_end);
+        for (int q = tid; q < (z1 - z0) * 16; q += 256) {
+            bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(z0 + (q >> 4)) * ld_out;
+            *reinterpret_cast<uint4*>(hrow + wt * (kTW / 2) + 8 * (q & 15)) = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+// ---- Which tile a workgroup computes.  Workgroup b runs on XCD b % 8 and is
+// that XCD's (b / 8)-th; an XCD's workgroups are dispatched in that order to
+// its 32 CUs.  Both schemes below enumerate only the tiles the segments hold.
+// Within one expert the tiles of a set of weight tiles are taken in groups of
+// gn weight tiles x all of the expert's ntt token tiles, token-major, with
+// gn ~ 32 / ntt: the ~32 tiles an XCD runs at once then read the same few
+// weight and token tiles, so each k-slice comes from HBM once and from the
+// XCD's L2 after that (measured on MI355X: with every tile's data L2-resident
+// the kernels ran 16% (gate/up) and 35% (down) faster than with an order that
+// let a round straddle two experts).
+struct TileId {
+    int split, e, ttl, wt;
+};
+
+// Down projection: XCD x takes the x-th of 8 equal contiguous runs of the
+// expert-major enumeration (K part, expert, group).  The token side (h rows,
+// 28 KB each) is then read by one or two XCDs only.
+__device__ __forceinline__ bool tile_contiguous(const int32_t* offsets, const int32_t* counts, int n_exp,
+                                                int n_wt, int ksplit, int tail_rows, TileId& t) {
+    int per_split = 0;
+    for (int j = 0; j < n_exp; ++j) per_split += token_tiles(offsets[j + 1] - offsets[j], counts[j], tail_rows) * n_wt;
+    const int total = per_split * ksplit;
+    const int run = (total + 7) >> 3;
+    if (static_cast<int>(blockIdx.x >> 3) >= run) return false;
+    const int L_all = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
+    if (L_all >= total) return false;
+    t.split = L_all / per_split;
+    int L = L_all - t.split * per_split;
+    int e = 0, ntt = 0;
+    for (; e < n_exp; ++e) {
+        ntt = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
+        if (L < ntt * n_wt) break;
+        L -= ntt * n_wt;
+    }
+    if (e == n_exp) return false;
+    const int gn = max(1, min(n_wt, kXcdTiles / ntt));
+    const int g = L / (gn * ntt);
+    const int rem = L - g * gn * ntt;
+    const int gw = min(gn, n_wt - g * gn);  // the last group may be narrower
+    t.e = e;
+    t.ttl = rem / gw;
+    t.wt = g * gn + (rem - t.ttl * gw);
+    return true;
+}
+
+// Gate/up: the weight tiles ("columns", numbered c = (K part * n_exp + e) *
+// n_wt + wt) are dealt to the XCDs, column c to XCD c % 8, each with all of
+// its expert's token tiles.  Every XCD then gets the same mix of every
+// expert's tiles, so the narrow tiles of the experts with short tails (cheaper
+// than full ones) are spread evenly: with contiguous runs, half of the XCDs
+// got none of them and ran 15% more full tiles than the others.  A column's
+// tiles stay on one XCD, so the weights keep their L2 reuse; the gathered
+// token rows (x is 32 MB) are read by every XCD.  An XCD holds at most
+// ceil(n_wt / 8) columns of an expert: its count exceeds total / 8 by at most
+// the number of token tiles, which the grid allows for.
+__device__ __forceinline__ bool tile_by_column(const int32_t* offsets, const int32_t* counts, int n_exp,
+                                               int n_wt, int ksplit, int tail_rows, TileId& t) {
+    const int x = blockIdx.x & 7;
+    int i = blockIdx.x >> 3;
+    int ntt = 0, first = 0, k = 0;
+    bool hit = false;
+    for (int se = 0; se < ksplit * n_exp; ++se) {
+        const int e = se % n_exp;
+        ntt = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
+        first = (x - (se * n_wt) % 8 + 8) % 8;                 // first weight tile of this XCD
+        k = first < n_wt ? (n_wt - 1 - first) / 8 + 1 : 0;     // its weight tiles of expert e
+        if (i < k * ntt) {
+            t.split = se / n_exp;
+            t.e = e;
+            hit = true;
+            break;
+        }
+        i -= k * ntt;
+    }
+    if (!hit) return false;
+    const int gn = max(1, min(k, kXcdTiles / ntt));
+    const int g = i / (gn * ntt);
+    const int rem = i - g * gn * ntt;
+    const int gw = min(gn, k - g * gn);
+    t.ttl = rem / gw;
+    t.wt = first + 8 * (g * gn + (rem - t.ttl * gw));
+    return true;
+}
+
 // PREACT (with DUAL): store the pre-activations a1 = w1 . x and a3 = w3 . x
 // in fp32 (out [P, 2 Nw]: a1 in columns 0..Nw-1, a3 after) instead of h, for
 // the backward pass.
@@ -234,38 +548,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ uint4 b0[kBufVec];
     __shared__ uint4 b1[kBufVec];
 
-    // ---- tile of this workgroup.  The grid covers the worst case (P_max / 256
-    // token tiles x n_wt per K part); the segments hold fewer.  Those tiles are dealt out
-    // evenly: XCD x (workgroups b with b % 8 == x) takes a contiguous run of
-    // ceil(total / 8) of them, and the remaining workgroups exit here.
+    // ---- tile of this workgroup (the grid covers the worst case; spare
+    // workgroups exit here)
     if (tail_rows > 0 && !tail_split_pays(offsets, counts, n_exp, n_wt * ksplit)) tail_rows = 0;
-    int per_split = 0;
-    for (int j = 0; j < n_exp; ++j) per_split += token_tiles(offsets[j + 1] - offsets[j], counts[j], tail_rows) * n_wt;
-    const int total = per_split * ksplit;
-    const int run = (total + 7) >> 3;
-    if (static_cast<int>(blockIdx.x >> 3) >= run) return;
-    const int L_all = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
-    if (L_all >= total) return;
-    const int split = L_all / per_split;
-    int L = L_all - split * per_split;
+    TileId t;
+    if (!(DUAL ? tile_by_column(offsets, counts, n_exp, n_wt, ksplit, tail_rows, t)
+               : tile_contiguous(offsets, counts, n_exp, n_wt, ksplit, tail_rows, t)))
+        return;
+    const int split = t.split, e = t.e, ttl = t.ttl, wt = t.wt;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
     out = static_cast<char*>(out) + split * split_stride * (DUAL && !PREACT ? sizeof(bf16_t) : sizeof(float));
-    // expert e owns tiles [sum of earlier experts' n_tt_e * n_wt, + n_tt_e * n_wt)
-    int e = 0, ntt_e = 0;
-    for (; e < n_exp; ++e) {
-        ntt_e = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
-        if (L < ntt_e * n_wt) break;
-        L -= ntt_e * n_wt;
-    }
-    if (e == n_exp) return;
-    // groups of gn weight tiles x the expert's ntt_e token tiles, token-major
-    const int gn = max(1, min(n_wt, kXcdTiles / ntt_e));
-    const int g = L / (gn * ntt_e);
-    const int rem = L - g * gn * ntt_e;
-    const int gw = min(gn, n_wt - g * gn);  // the last group may be narrower
-    const int ttl = rem / gw;
-    const int wt = g * gn + (rem - ttl * gw);
 
     const int p0 = offsets[e] + ttl * kTT;
     const int row_end = min(offsets[e + 1], P);
@@ -328,6 +621,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int q = 0; q < 4; ++q) c.rd[q] = row0 * kChunks + ((2 * q + fk) ^ swz(fr));
         c.rdt = (kTW + wave_t * 128 - wave_w * (DUAL ? 64 : 128)) * kChunks;
+    }
+
+    if (!PREACT && valid <= 128) {
+        if (valid <= 64)
+            narrow_tile<DUAL, 2>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
+                                 valid, row_end);
+        else
+            narrow_tile<DUAL, 4>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
+                                 valid, row_end);
+        return;
     }
 
     f32x16_t acc[4][4];
@@ -435,7 +738,8 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = gate_up ? s.F / (kTW / 2) : s.d / kTW;
-    const int G = (n_tt * n_wt * ksplit + 7) / 8 * 8;
+    // gate/up: an XCD may hold up to n_tt * ksplit tiles more than an eighth
+    const int G = ((n_tt * n_wt * ksplit + 7) / 8 + (gate_up ? n_tt * ksplit : 0)) * 8;
     const size_t split_stride = static_cast<size_t>(P) * (gate_up ? s.F : s.d);
     if (gate_up)
         tiled_kernel<true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(act), row_src, counts, offsets,
@@ -455,7 +759,7 @@ hipError_t launch_tiled_preact(const Shape& s, const void* x, const int32_t* row
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = s.F / (kTW / 2);
-    const int G = (n_tt * n_wt + 7) / 8 * 8;
+    const int G = ((n_tt * n_wt + 7) / 8 + n_tt) * 8;
     tiled_kernel<true, true><<<G, 256, 0, st>>>(static_cast<const bf16_t*>(x), row_src, counts, offsets,
                                                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3), a,
                                                 s.d, s.F, s.d, n_wt, 2 * s.F, s.T * s.K, P, 1, 0, s.n, s.K, 0);
