@@ -229,7 +229,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
         if (r == 0 || r > tail_rows) return;
         // the same decision as the tiled kernel's: gridDim.x is Nw / 64 here, the
         // tiled kernel's weight tiles of 256 rows are Nw / 256, times its K parts
-        if (!tail_split_pays(offsets, counts, gridDim.y, Nw / kTiledRows * tail_parts)) return;
+        Segments sg;
+        load_segments(offsets, counts, gridDim.y, sg);
+        if (!tail_split_pays(sg, gridDim.y, Nw / kTiledRows * tail_parts)) return;
         seg += cnt - r;
         cnt = r;
         if (DUAL) {

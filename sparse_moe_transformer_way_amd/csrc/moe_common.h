@@ -67,7 +67,6 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 // Internal launchers (host side).  Each enqueues on `stream` and returns the
 // hipGetLastError() status of its launches.  Shapes are validated by the ABI.
 // ---------------------------------------------------------------------------
-// Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
 // Token rows of a tile of the LDS-tiled MFMA kernels, and the largest
 // remainder of an expert's rows (past its full tiles) that the weight-streaming
 // kernels take over from them in the tile-256 layout: such a tail would cost a
@@ -76,26 +75,46 @@ constexpr int kTiledRows = 256;
 constexpr int kTailRows = 64;
 constexpr int kComputeUnits = 256;  // MI355X: a round of tiled-kernel tiles
 
+// Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
+constexpr int kMaxExperts = 16;
+constexpr int kMaxTopK = 4;
+
+// Every expert's segment offset and count.  All loads are issued before any is
+// used (indices clamped into the arrays), so a kernel's prologue waits one
+// memory latency for them, not one per expert as a loop that loads as it goes.
+struct Segments {
+    int off[kMaxExperts + 1];
+    int cnt[kMaxExperts];
+};
+
+__device__ __forceinline__ void load_segments(const int32_t* offsets, const int32_t* counts, int n_exp,
+                                              Segments& s) {
+#pragma unroll
+    for (int j = 0; j <= kMaxExperts; ++j) s.off[j] = offsets[min(j, n_exp)];
+#pragma unroll
+    for (int j = 0; j < kMaxExperts; ++j) s.cnt[j] = counts[min(j, n_exp - 1)];
+}
+
 // Whether moving the short tails out of the tiled kernel saves it a round of
 // tiles: ceil(tiles / CUs) drops.  Both the tiled kernel and the streaming
 // tail pass evaluate this from the same device-side counts, so they agree.
 // tiles_per_row_tile: tiles of one 256-row token tile (weight tiles x K parts).
-__device__ __forceinline__ bool tail_split_pays(const int32_t* offsets, const int32_t* counts, int n_exp,
-                                                int tiles_per_row_tile) {
+__device__ __forceinline__ bool tail_split_pays(const Segments& s, int n_exp, int tiles_per_row_tile) {
     int with_tail = 0, without = 0;
-    for (int e = 0; e < n_exp; ++e) {
-        const int len = offsets[e + 1] - offsets[e];
-        const int c = counts[e];
-        const int r = c % kTiledRows;
-        without += len / kTiledRows;
-        with_tail += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+        if (e < n_exp) {
+            const int len = s.off[e + 1] - s.off[e];
+            const int c = s.cnt[e];
+            const int r = c % kTiledRows;
+            without += len / kTiledRows;
+            with_tail += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
+        }
     }
     const int per_round = kComputeUnits;
     return (with_tail * tiles_per_row_tile + per_round - 1) / per_round <
            (without * tiles_per_row_tile + per_round - 1) / per_round;
 }
-constexpr int kMaxExperts = 16;
-constexpr int kMaxTopK = 4;
 
 struct Shape {
     int T, d, F, n, K;  // n <= kMaxExperts, K <= min(n, kMaxTopK)

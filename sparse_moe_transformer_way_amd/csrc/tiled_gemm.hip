@@ -206,10 +206,11 @@ __device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__
 }
 
 // The K loop over nb blocks (nb a multiple of 4, >= 4).  Before it: blocks 0
-// and 1 are being copied into b0 and b1.
+// and 1 are being copied into b0 and b1, the weights of both first, then the
+// tokens of block 0, then those of block 1.
 template <bool DUAL, bool ACTIVE>
 __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1, int nb, f32x16_t (&acc)[4][4]) {
-    block_barrier<kCopies>();  // block 0 has landed
+    block_barrier<kCopies / 2>();  // block 0 has landed (block 1's token copies may not have)
     Frag16 f0, f1;
     if (ACTIVE) read_half<DUAL>(c, b0, 0, f0);
     int kb = 0;
@@ -339,21 +340,31 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
     const int fk = lane >> 5;
     const int rl = lane >> 3;
 
+    // token copy group jj of wave w fills token rows r = w * TN/4 + 8 jj + l/8.
+    // As in the full tile: the row loads, then the weight copies of blocks 0
+    // and 1, which do not wait for them.
+    const int r0 = wave * (TN / 4);
+    int srcs[TB];
+    if (DUAL) {
+#pragma unroll
+        for (int jj = 0; jj < TB; ++jj) srcs[jj] = row_src[p0 + min(r0 + 8 * jj + rl, valid - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b0, 0, j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b1, kBK, j);
+
     NarrowCtx n;
     {
-        // token copy group jj of wave w fills token rows r = w * TN/4 + 8 jj + l/8;
         // bit 4 of r (the only bit of g(r) above the row-in-group bits) is fixed per group
         const int ch0 = (lane & 7) ^ swz(rl);
         const int ch1 = (lane & 7) ^ swz(16 + rl);
-        const int r0 = wave * (TN / 4);
         if (DUAL) {
             n.tres = make_rsrc(act + kbase);
-            const int first_src = row_src[p0];
 #pragma unroll
             for (int jj = 0; jj < TB; ++jj) {
-                const int r = r0 + 8 * jj + rl;
-                int src = (r < valid) ? row_src[p0 + r] : first_src;
-                if (src < 0 || src >= n_src) src = first_src;
+                int src = srcs[jj];
                 if (src < 0 || src >= n_src) src = 0;
                 const int ch = (((r0 + 8 * jj) >> 4) & 1) ? ch1 : ch0;
                 n.to[jj] = static_cast<uint32_t>(
@@ -387,10 +398,10 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
 
     const int nb = kpart / kBK;  // a multiple of 4, >= 4
 #pragma unroll
-    for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b0, 0, j);
+    for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b0, 0, j);
 #pragma unroll
-    for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b1, kBK, j);
-    block_barrier<8 + TB>();  // block 0 has landed
+    for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b1, kBK, j);
+    block_barrier<TB>();  // block 0 has landed (block 1's token copies may not have)
     u32x4_t f0[2 * (2 + TB)], f1[2 * (2 + TB)];
     read_narrow<TB>(n, b0, 0, f0);
     int kb = 0;
@@ -463,15 +474,21 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
 // let a round straddle two experts).
 struct TileId {
     int split, e, ttl, wt;
+    int seg, seg_end, cnt;  // the expert's segment: offsets[e], offsets[e + 1], counts[e]
 };
 
 // Down projection: XCD x takes the x-th of 8 equal contiguous runs of the
 // expert-major enumeration (K part, expert, group).  The token side (h rows,
 // 28 KB each) is then read by one or two XCDs only.
-__device__ __forceinline__ bool tile_contiguous(const int32_t* offsets, const int32_t* counts, int n_exp,
-                                                int n_wt, int ksplit, int tail_rows, TileId& t) {
+__device__ __forceinline__ bool tile_contiguous(const Segments& sg, int n_exp, int n_wt, int ksplit, int tail_rows,
+                                                TileId& t) {
+    int ntt[kMaxExperts];
     int per_split = 0;
-    for (int j = 0; j < n_exp; ++j) per_split += token_tiles(offsets[j + 1] - offsets[j], counts[j], tail_rows) * n_wt;
+#pragma unroll
+    for (int j = 0; j < kMaxExperts; ++j) {
+        ntt[j] = j < n_exp ? token_tiles(sg.off[j + 1] - sg.off[j], sg.cnt[j], tail_rows) : 0;
+        per_split += ntt[j] * n_wt;
+    }
     const int total = per_split * ksplit;
     const int run = (total + 7) >> 3;
     if (static_cast<int>(blockIdx.x >> 3) >= run) return false;
@@ -479,18 +496,28 @@ __device__ __forceinline__ bool tile_contiguous(const int32_t* offsets, const in
     if (L_all >= total) return false;
     t.split = L_all / per_split;
     int L = L_all - t.split * per_split;
-    int e = 0, ntt = 0;
-    for (; e < n_exp; ++e) {
-        ntt = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
-        if (L < ntt * n_wt) break;
-        L -= ntt * n_wt;
+    int nt = 0;
+    bool hit = false;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+        if (!hit && e < n_exp) {
+            if (L < ntt[e] * n_wt) {
+                hit = true;
+                t.e = e;
+                nt = ntt[e];
+                t.seg = sg.off[e];
+                t.seg_end = sg.off[e + 1];
+                t.cnt = sg.cnt[e];
+            } else {
+                L -= ntt[e] * n_wt;
+            }
+        }
     }
-    if (e == n_exp) return false;
-    const int gn = max(1, min(n_wt, kXcdTiles / ntt));
-    const int g = L / (gn * ntt);
-    const int rem = L - g * gn * ntt;
+    if (!hit) return false;
+    const int gn = max(1, min(n_wt, kXcdTiles / nt));
+    const int g = L / (gn * nt);
+    const int rem = L - g * gn * nt;
     const int gw = min(gn, n_wt - g * gn);  // the last group may be narrower
-    t.e = e;
     t.ttl = rem / gw;
     t.wt = g * gn + (rem - t.ttl * gw);
     return true;
@@ -505,30 +532,41 @@ __device__ __forceinline__ bool tile_contiguous(const int32_t* offsets, const in
 // tiles stay on one XCD, so the weights keep their L2 reuse; the gathered
 // token rows (x is 32 MB) are read by every XCD.  An XCD holds at most
 // ceil(n_wt / 8) columns of an expert: its count exceeds total / 8 by at most
-// the number of token tiles, which the grid allows for.
-__device__ __forceinline__ bool tile_by_column(const int32_t* offsets, const int32_t* counts, int n_exp,
-                                               int n_wt, int ksplit, int tail_rows, TileId& t) {
+// the number of token tiles, which the grid allows for.  ksplit <= 2.
+__device__ __forceinline__ bool tile_by_column(const Segments& sg, int n_exp, int n_wt, int ksplit, int tail_rows,
+                                               TileId& t) {
     const int x = blockIdx.x & 7;
     int i = blockIdx.x >> 3;
-    int ntt = 0, first = 0, k = 0;
+    int nt = 0, first = 0, k = 0;
     bool hit = false;
-    for (int se = 0; se < ksplit * n_exp; ++se) {
-        const int e = se % n_exp;
-        ntt = token_tiles(offsets[e + 1] - offsets[e], counts[e], tail_rows);
-        first = (x - (se * n_wt) % 8 + 8) % 8;                 // first weight tile of this XCD
-        k = first < n_wt ? (n_wt - 1 - first) / 8 + 1 : 0;     // its weight tiles of expert e
-        if (i < k * ntt) {
-            t.split = se / n_exp;
-            t.e = e;
-            hit = true;
-            break;
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e) {
+            if (!hit && sp < ksplit && e < n_exp) {
+                const int ntt = token_tiles(sg.off[e + 1] - sg.off[e], sg.cnt[e], tail_rows);
+                const int f = (x - ((sp * n_exp + e) * n_wt) % 8 + 8) % 8;  // this XCD's first weight tile
+                const int kk = f < n_wt ? (n_wt - 1 - f) / 8 + 1 : 0;      // its weight tiles of expert e
+                if (i < kk * ntt) {
+                    hit = true;
+                    t.split = sp;
+                    t.e = e;
+                    t.seg = sg.off[e];
+                    t.seg_end = sg.off[e + 1];
+                    t.cnt = sg.cnt[e];
+                    nt = ntt;
+                    first = f;
+                    k = kk;
+                } else {
+                    i -= kk * ntt;
+                }
+            }
         }
-        i -= k * ntt;
     }
     if (!hit) return false;
-    const int gn = max(1, min(k, kXcdTiles / ntt));
-    const int g = i / (gn * ntt);
-    const int rem = i - g * gn * ntt;
+    const int gn = max(1, min(k, kXcdTiles / nt));
+    const int g = i / (gn * nt);
+    const int rem = i - g * gn * nt;
     const int gw = min(gn, k - g * gn);
     t.ttl = rem / gw;
     t.wt = first + 8 * (g * gn + (rem - t.ttl * gw));
@@ -550,19 +588,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- tile of this workgroup (the grid covers the worst case; spare
     // workgroups exit here)
-    if (tail_rows > 0 && !tail_split_pays(offsets, counts, n_exp, n_wt * ksplit)) tail_rows = 0;
+    Segments sg;
+    load_segments(offsets, counts, n_exp, sg);
+    if (tail_rows > 0 && !tail_split_pays(sg, n_exp, n_wt * ksplit)) tail_rows = 0;
     TileId t;
-    if (!(DUAL ? tile_by_column(offsets, counts, n_exp, n_wt, ksplit, tail_rows, t)
-               : tile_contiguous(offsets, counts, n_exp, n_wt, ksplit, tail_rows, t)))
+    if (!(DUAL ? tile_by_column(sg, n_exp, n_wt, ksplit, tail_rows, t)
+               : tile_contiguous(sg, n_exp, n_wt, ksplit, tail_rows, t)))
         return;
     const int split = t.split, e = t.e, ttl = t.ttl, wt = t.wt;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
     out = static_cast<char*>(out) + split * split_stride * (DUAL && !PREACT ? sizeof(bf16_t) : sizeof(float));
 
-    const int p0 = offsets[e] + ttl * kTT;
-    const int row_end = min(offsets[e + 1], P);
-    const int valid = min(min(kTT, offsets[e] + counts[e] - p0), row_end - p0);
+    const int p0 = t.seg + ttl * kTT;
+    const int row_end = min(t.seg_end, P);
+    const int valid = min(min(kTT, t.seg + t.cnt - p0), row_end - p0);
     if (valid <= 0) return;
 
     const int tid = threadIdx.x;
@@ -573,15 +613,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int fr = lane & 31;  // fragment row / token column of this lane
     const int fk = lane >> 5;  // k-group of this lane within a k16 half
 
+    // Copies: wave w fills LDS rows w*64 .. +64 of the weight half and of the
+    // token half as 8 groups of 8 rows; lane l of group j writes row
+    // w*64 + 8j + l/8, physical chunk l%8, so it reads logical chunk
+    // (l%8) ^ g(row).  g() of that row depends on l and on j's bit 1 only.
+    const int rl = lane >> 3;
+    const int ch0 = (lane & 7) ^ swz(rl);
+    const int ch1 = (lane & 7) ^ swz(16 + rl);
     TileCtx c;
     {
-        // Copies: wave w fills LDS rows w*64 .. +64 of the weight half and of
-        // the token half as 8 groups of 8 rows; lane l of group j writes row
-        // w*64 + 8j + l/8, physical chunk l%8, so it reads logical chunk
-        // (l%8) ^ g(row).  g() of that row depends on l and on j's bit 1 only.
-        const int rl = lane >> 3;
-        const int ch0 = (lane & 7) ^ swz(rl);
-        const int ch1 = (lane & 7) ^ swz(16 + rl);
         // Gate/up: LDS weight rows 0-127 (waves 0, 1) are w1 rows, 128-255
         // (waves 2, 3) the same rows of w3.
         const bf16_t* wm = (DUAL && wave >= 2) ? wb : wa;
@@ -590,15 +630,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         c.wo[0] = (static_cast<uint32_t>(rl) * Kdim + 8u * ch0) * 2u;
         c.wo[1] = (static_cast<uint32_t>(rl) * Kdim + 8u * ch1) * 2u;
         c.wstride = 8 * Kdim * 2;
+        c.dma = wave * 64 * kChunks;
+    }
+
+    if (!PREACT && valid <= 128) {
+        if (valid <= 64)
+            narrow_tile<DUAL, 2>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
+                                 valid, row_end);
+        else
+            narrow_tile<DUAL, 4>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
+                                 valid, row_end);
+        return;
+    }
+
+    // Gate/up: the rows of x this lane copies (padding rows copy the tile's
+    // last real row).  The loads are unconditional, so all eight are in flight
+    // at once, and they go out ahead of the weight copies of blocks 0 and 1,
+    // which do not depend on them: waiting for these loads leaves the copies
+    // in flight.
+    int srcs[8];
+    if (DUAL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) srcs[j] = row_src[p0 + min(wave * 64 + 8 * j + rl, valid - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b0, 0, j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b1, kBK, j);
+    {
         if (DUAL) {
-            // gathered rows of x; padding rows copy the tile's first row
             c.tres = make_rsrc(act + kbase);
-            const int first_src = row_src[p0];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int r = wave * 64 + 8 * j + rl;
-                int src = (r < valid) ? row_src[p0 + r] : first_src;
-                if (src < 0 || src >= n_src) src = first_src;
+                int src = srcs[j];
                 if (src < 0 || src >= n_src) src = 0;
                 c.to[j] = static_cast<uint32_t>(
                     (static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
@@ -614,23 +679,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 2; j < 8; ++j) c.to[j] = 0;
             c.tstride = 8 * ld_act * 2;
         }
-        c.dma = wave * 64 * kChunks;
         // Fragment reads: blocks start at multiples of 32 rows, so g() of a
         // block row is g(fr).  Logical chunk of half s, k16 half h: 4s + 2h + fk.
         const int row0 = wave_w * (DUAL ? 64 : 128) + fr;
 #pragma unroll
         for (int q = 0; q < 4; ++q) c.rd[q] = row0 * kChunks + ((2 * q + fk) ^ swz(fr));
         c.rdt = (kTW + wave_t * 128 - wave_w * (DUAL ? 64 : 128)) * kChunks;
-    }
-
-    if (!PREACT && valid <= 128) {
-        if (valid <= 64)
-            narrow_tile<DUAL, 2>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
-                                 valid, row_end);
-        else
-            narrow_tile<DUAL, 4>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
-                                 valid, row_end);
-        return;
     }
 
     f32x16_t acc[4][4];
@@ -643,9 +697,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int nb = kpart / kBK;  // a multiple of 4, >= 4 (K parts are multiples of 256)
 #pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, b0, 0, j);
+    for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b0, 0, j);
 #pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
+    for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
     // A wave whose 128 token rows are all padding skips its reads and MFMAs.
     if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0)
         main_loop<DUAL, true>(c, b0, b1, nb, acc);
@@ -734,7 +788,7 @@ int tiled_down_ksplit(const Shape& s) {
 hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int32_t* row_src,
                         const int32_t* counts, const int32_t* offsets, const void* wa, const void* wb,
                         void* out, hipStream_t st, int ksplit, int tail_rows) {
-    if (!tiled_fits(s)) return hipErrorInvalidValue;
+    if (!tiled_fits(s) || ksplit < 1 || ksplit > 2) return hipErrorInvalidValue;
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = gate_up ? s.F / (kTW / 2) : s.d / kTW;
