@@ -180,6 +180,48 @@ def test_grouped_swiglu(dtype, T, d, F, tile_m):
             assert per_token_rel_err(yp2_np[rows], exp).max() <= (1e-5 if dtype == "f32" else 1e-4)
 
 
+# Per-expert row counts on both sides of the tiled kernels' tile shapes: an
+# expert's last 256-row tile runs as a 64-row tile up to 64 real rows, as a
+# 128-row tile up to 128, and as a full tile above (64, 65, 128, 129 alone and
+# past one full tile).  The assignments are placed directly, not routed.
+NARROW_COUNTS = [64, 65, 128, 129, 320, 321, 384, 385]
+
+
+@pytest.mark.parametrize("counts_target", [NARROW_COUNTS, NARROW_COUNTS[::-1], [1, 2, 63, 127, 255, 257, 0, 130]])
+def test_grouped_swiglu_tile_shape_boundaries(counts_target):
+    d, F = 512, 1024
+    flat = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts_target)])
+    rng = np.random.default_rng(len(flat))
+    flat = flat[rng.permutation(flat.size)]
+    if flat.size % 2:
+        flat = np.concatenate([flat, np.array([-1], np.int32)])  # one assignment to no expert
+    idx = flat.reshape(-1, 2)
+    T = idx.shape[0]
+    inp = mi.make_layer(T, d, F, seed=T, workload=204)
+    xn, _, w1n, w3n, w2n = inp.numpy_f32()
+    valid = idx >= 0
+    grp = oracle.group_by_expert(np.where(valid, idx, 8), 9, 256)  # the -1 goes to a ninth, dropped expert
+    P = moe.moe_max_permuted_rows(moe.make_desc(d, F), T, 256)
+    offsets = grp["offsets"][:9]
+    row_src = np.full(P, -1, np.int32)
+    row_src[:offsets[8]] = grp["row_src"][:offsets[8]]
+    counts = grp["counts"][:8]
+    np.testing.assert_array_equal(counts, counts_target)
+    h_ref, yp_ref = oracle.expert_rows(xn, row_src, offsets, w1n, w3n, w2n)
+    desc = moe.make_desc(d, F)
+    h, yp = moe.moe_grouped_swiglu(desc, T, 256, inp.x.cuda(), torch.from_numpy(row_src).cuda(),
+                                   torch.from_numpy(counts).cuda(), torch.from_numpy(offsets).cuda(),
+                                   inp.w1.cuda(), inp.w3.cuda(), inp.w2.cuda())
+    torch.cuda.synchronize()
+    real = row_src >= 0
+    pad = ~real
+    pad[offsets[8]:] = False
+    hg = h.float().cpu().numpy()
+    assert per_token_rel_err(hg[real], h_ref[real]).max() <= TOL_BF16
+    assert per_token_rel_err(yp.cpu().numpy()[real], yp_ref[real]).max() <= TOL_BF16
+    assert (hg[pad] == 0).all()
+
+
 def test_grouped_swiglu_empty_and_full_experts():
     """All tokens on experts 2 and 5, six experts with no rows."""
     T, d, F = 300, 512, 1024
