@@ -424,6 +424,7 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
             bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
             const int fb = wt * (kTW / 2) + 32 * wave;
             const uint32_t keep = real ? 0xffffffffu : 0u;
+            uint2 o[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 float v[4];
@@ -432,10 +433,15 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
                     const float hv = silu_f32(acc[0][i][4 * q4 + u]) * acc[1][i][4 * q4 + u];
                     v[u] = __uint_as_float(__float_as_uint(hv) & keep);
                 }
-                uint2 o;
-                o.x = pack_bf16x2(v[0], v[1]);
-                o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(hrow + fb + 8 * q4 + 4 * fk) = o;
+                o[q4].x = pack_bf16x2(v[0], v[1]);
+                o[q4].y = pack_bf16x2(v[2], v[3]);
+            }
+            // 16-byte stores after a permlane32 swap, as in the full tile
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const auto sx = __builtin_amdgcn_permlane32_swap(o[2 * pr].x, o[2 * pr + 1].x, false, false);
+                const auto sy = __builtin_amdgcn_permlane32_swap(o[2 * pr].y, o[2 * pr + 1].y, false, false);
+                *reinterpret_cast<uint4*>(hrow + fb + 8 * (2 * pr + fk)) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
             }
         } else {
             if (!real) continue;
@@ -740,6 +746,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint32_t keep = real ? 0xffffffffu : 0u;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
+                uint2 o[4];  // the lane's 4 h values of each q4 (f = 8 q4 + 4 fk + u), bf16
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     float v[4];
@@ -748,10 +755,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         const float hv = silu_f32(acc[jj][i][4 * q4 + u]) * acc[jj + 2][i][4 * q4 + u];
                         v[u] = __uint_as_float(__float_as_uint(hv) & keep);
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(hrow + fb + jj * 32 + 8 * q4 + 4 * fk) = o;
+                    o[q4].x = pack_bf16x2(v[0], v[1]);
+                    o[q4].y = pack_bf16x2(v[2], v[3]);
+                }
+                // Lanes l and l + 32 hold the two halves of each 8-wide run of f
+                // of the same row.  v_permlane32_swap hands lane l its partner's
+                // half of the even runs and lane l + 32 lane l's half of the odd
+                // ones (measured on gfx950), so each lane stores 16 bytes: run
+                // 2 pr + fk, half the store instructions of 8-byte stores.
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const auto sx = __builtin_amdgcn_permlane32_swap(o[2 * pr].x, o[2 * pr + 1].x, false, false);
+                    const auto sy = __builtin_amdgcn_permlane32_swap(o[2 * pr].y, o[2 * pr + 1].y, false, false);
+                    *reinterpret_cast<uint4*>(hrow + fb + jj * 32 + 8 * (2 * pr + fk)) =
+                        make_uint4(sx[0], sy[0], sx[1], sy[1]);
                 }
             }
         } else {
