@@ -276,7 +276,7 @@ struct GemmArgs {
     int ldc;
     int csplit;             // v where c1 takes over (kEpiDw), else 0
     // kEpiGrad
-    const float* a;         // [P, 2F] pre-activations (fp32)
+    const float* a;         // [P, 2F] pre-activations (fp32, 32 x 32 blocks: preact_block)
     const float* gp;        // [P] gate of each row (0 for padding)
     bf16_t* hg;             // [P, F]
     float* dgp;             // [U / kTU, P] partial dg sums
@@ -461,22 +461,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // kEpiGrad: u = feature f of F, v = permuted row p.  With a1 = a[p][f],
         // a3 = a[p][F + f], gate gv:  h = SiLU(a1) a3, dg += G h,
         // da3 = gv G SiLU(a1), da1 = gv G a3 SiLU'(a1), hg = gv h.
+        // a is read in its 32 x 32 blocks (preact_block), which follow this C
+        // layout: the lane's 16 values of a block are contiguous.
         const int F = g.U;
         float dg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int bv = 0; bv < 4; ++bv) {
             const int p = v0 + wv * 128 + bv * 32 + (lane & 31);
+            const int pb = (v0 + wv * 128 + bv * 32) / 32;
             const float gv = g.gp[p];
-            const float* arow = g.a + static_cast<int64_t>(p) * 2 * F;
             bf16_t* darow = static_cast<bf16_t*>(g.c0) + static_cast<int64_t>(p) * 2 * F;
             bf16_t* hrow = g.hg + static_cast<int64_t>(p) * F;
 #pragma unroll
-            for (int bu = 0; bu < 4; ++bu)
+            for (int bu = 0; bu < 4; ++bu) {
+                const int fbk = (u0 + wu * 128 + bu * 32) / 32;
+                const float* a1b = g.a + preact_block(pb, fbk, F) + lane * 16;
+                const float* a3b = g.a + preact_block(pb, fbk + F / 32, F) + lane * 16;
+                uint2 o1[4], o3[4], oh[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int f = u0 + wu * 128 + bu * 32 + 8 * q4 + 4 * fk;
-                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(arow + f);
-                    const f32x4_t a3 = *reinterpret_cast<const f32x4_t*>(arow + F + f);
+                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(a1b + 4 * q4);
+                    const f32x4_t a3 = *reinterpret_cast<const f32x4_t*>(a3b + 4 * q4);
                     float d1[4], d3[4], hv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -490,17 +495,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         d1[i] = dh * a3[i] * (sg * (1.0f + a1[i] * (1.0f - sg)));
                         hv[i] = gv * h;
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(d1[0], d1[1]);
-                    o.y = pack_bf16x2(d1[2], d1[3]);
-                    *reinterpret_cast<uint2*>(darow + f) = o;
-                    o.x = pack_bf16x2(d3[0], d3[1]);
-                    o.y = pack_bf16x2(d3[2], d3[3]);
-                    *reinterpret_cast<uint2*>(darow + F + f) = o;
-                    o.x = pack_bf16x2(hv[0], hv[1]);
-                    o.y = pack_bf16x2(hv[2], hv[3]);
-                    *reinterpret_cast<uint2*>(hrow + f) = o;
+                    o1[q4].x = pack_bf16x2(d1[0], d1[1]);
+                    o1[q4].y = pack_bf16x2(d1[2], d1[3]);
+                    o3[q4].x = pack_bf16x2(d3[0], d3[1]);
+                    o3[q4].y = pack_bf16x2(d3[2], d3[3]);
+                    oh[q4].x = pack_bf16x2(hv[0], hv[1]);
+                    oh[q4].y = pack_bf16x2(hv[2], hv[3]);
                 }
+                // Lanes l and l + 32 hold the two halves of each 8-wide run of f
+                // of row p; after a v_permlane32_swap each lane stores a whole
+                // run (run 2 pr + fk) in 16 bytes.
+                const int fr0 = u0 + wu * 128 + bu * 32;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int f8 = fr0 + 8 * (2 * pr + fk);
+                    auto sx = __builtin_amdgcn_permlane32_swap(o1[2 * pr].x, o1[2 * pr + 1].x, false, false);
+                    auto sy = __builtin_amdgcn_permlane32_swap(o1[2 * pr].y, o1[2 * pr + 1].y, false, false);
+                    *reinterpret_cast<uint4*>(darow + f8) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                    sx = __builtin_amdgcn_permlane32_swap(o3[2 * pr].x, o3[2 * pr + 1].x, false, false);
+                    sy = __builtin_amdgcn_permlane32_swap(o3[2 * pr].y, o3[2 * pr + 1].y, false, false);
+                    *reinterpret_cast<uint4*>(darow + F + f8) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                    sx = __builtin_amdgcn_permlane32_swap(oh[2 * pr].x, oh[2 * pr + 1].x, false, false);
+                    sy = __builtin_amdgcn_permlane32_swap(oh[2 * pr].y, oh[2 * pr + 1].y, false, false);
+                    *reinterpret_cast<uint4*>(hrow + f8) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                }
+            }
         }
         // dg partial over the block's 256 features, in a fixed order: the two
         // k-group lanes of a column, then the two u halves of the block

@@ -75,6 +75,18 @@ constexpr int kTiledRows = 256;
 constexpr int kTailRows = 64;
 constexpr int kComputeUnits = 256;  // MI355X: a round of tiled-kernel tiles
 
+// Layout of the backward pass's fp32 pre-activations a = [a1 | a3], logically
+// [P, 2F]: 32 x 32 blocks in the C layout of a 32x32 MFMA whose columns are the
+// rows p and whose rows are the features f.  Block (p / 32, f / 32) starts at
+// float (p / 32 * (2F / 32) + f / 32) * 1024; in it, lane l holds row p % 32 =
+// l % 32 and features 8 (q / 4) + 4 (l / 32) + q % 4, q = 0..15, as 16
+// contiguous floats from l * 16.  The kernel that writes a block and the one
+// that reads it move 64 contiguous bytes per lane (4 KB per wave), where rows of
+// [P, 2F] would take 32 rows x 32 bytes per instruction.
+__device__ __forceinline__ size_t preact_block(int pb, int fb, int F) {
+    return (static_cast<size_t>(pb) * (2 * F / 32) + fb) * 1024;
+}
+
 // Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
 constexpr int kMaxExperts = 16;
 constexpr int kMaxTopK = 4;
@@ -161,7 +173,7 @@ struct BackwardWs {
     bf16_t* xp;       // [P, d] gathered x
     bf16_t* dyp;      // [P, d] gathered dy
     float* gp;        // [P] gate of each row
-    float* a;         // [P, 2F] pre-activations a1 | a3
+    float* a;         // [P, 2F] pre-activations a1 | a3, in 32 x 32 blocks (preact_block)
     bf16_t* da;       // [P, 2F] their gradients
     bf16_t* hg;       // [P, F] gate * h
     float* dgp;       // [F / 256, P] partial gate gradients

@@ -580,8 +580,8 @@ __device__ __forceinline__ bool tile_by_column(const Segments& sg, int n_exp, in
 }
 
 // PREACT (with DUAL): store the pre-activations a1 = w1 . x and a3 = w3 . x
-// in fp32 (out [P, 2 Nw]: a1 in columns 0..Nw-1, a3 after) instead of h, for
-// the backward pass.
+// in fp32 (out [P, 2 Nw]: a1 in columns 0..Nw-1, a3 after, in the 32 x 32
+// blocks of preact_block) instead of h, for the backward pass.
 template <bool DUAL, bool PREACT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_kernel(
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
@@ -721,11 +721,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (p >= row_end) continue;
         const bool real = rt < valid;
         if (DUAL && PREACT) {
-            float* arow = static_cast<float*>(out) + static_cast<size_t>(p) * ld_out;
-            const int fb = wt * (kTW / 2) + wave_w * 64;
+            // a in 32 x 32 blocks (preact_block): this block's 16 values of
+            // the lane are contiguous
+            const int pb = (p0 + wave_t * 128 + i * 32) / 32;
+            const int fbk = (wt * (kTW / 2) + wave_w * 64) / 32;
             const uint32_t keep = real ? 0xffffffffu : 0u;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int jj = 0; jj < 2; ++jj) {
+                float* a1b = static_cast<float*>(out) + preact_block(pb, fbk + jj, Nw) + lane * 16;
+                float* a3b = static_cast<float*>(out) + preact_block(pb, fbk + jj + Nw / 32, Nw) + lane * 16;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     f32x4_t a1, a3;
@@ -734,10 +738,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         a1[u] = __uint_as_float(__float_as_uint(acc[jj][i][4 * q4 + u]) & keep);
                         a3[u] = __uint_as_float(__float_as_uint(acc[jj + 2][i][4 * q4 + u]) & keep);
                     }
-                    const int f = fb + jj * 32 + 8 * q4 + 4 * fk;
-                    *reinterpret_cast<f32x4_t*>(arow + f) = a1;
-                    *reinterpret_cast<f32x4_t*>(arow + Nw + f) = a3;
+                    *reinterpret_cast<f32x4_t*>(a1b + 4 * q4) = a1;
+                    *reinterpret_cast<f32x4_t*>(a3b + 4 * q4) = a3;
                 }
+            }
         } else if (DUAL) {
             bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * ld_out;
             const int fb = wt * (kTW / 2) + wave_w * 64;
