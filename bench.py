@@ -266,7 +266,7 @@ def bench_stack(args, spec):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch
