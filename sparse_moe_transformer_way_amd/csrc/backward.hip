@@ -288,44 +288,6 @@ struct GemmArgs {
     int64_t c_split_stride;
 };
 
-// Store a wave's 128 x 128 fp32 results (C layout: rows v = lane % 32 of each
-// 32-block, columns u = 8 (q / 4) + 4 (lane / 32) + q % 4) to dst[v][u] through
-// its stage buffer stg (32 KB, free after the K loop: every fragment read fed
-// an MFMA).  In the C layout a store instruction would write 32 rows x 32
-// bytes; staged, 64 rows at a time, each store writes 2 rows x 512 contiguous
-// bytes (measured: the scattered stores made the weight-gradient products
-// about a fifth slower).  LDS row r holds 128 floats as 32 chunks of 16 bytes,
-// chunk c at c ^ (r % 32): the 32 rows of a write instruction and the 32
-// chunks of a read hit distinct chunk slots.  LDS runs one wave's
-// instructions in order, so no barrier is needed between the writes and the
-// reads, nor between the two halves.
-__device__ __forceinline__ void store_rows_staged(const f32x16_t (&acc)[4][4], f32x4_t* stg, float* dst,
-                                                  int64_t ldc, int v_base, int u_base, int lane) {
-    const int fk = lane >> 5;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int r = b2 * 32 + (lane & 31);  // row within the half
-#pragma unroll
-            for (int bu = 0; bu < 4; ++bu)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x16_t& c = acc[bu][2 * half + b2];
-                    const int chunk = bu * 8 + 2 * q4 + fk;
-                    stg[r * 32 + (chunk ^ (r & 31))] = f32x4_t{c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int r = 2 * i + (lane >> 5);
-            const int chunk = lane & 31;
-            const f32x4_t o = stg[r * 32 + (chunk ^ (r & 31))];
-            *reinterpret_cast<f32x4_t*>(dst + static_cast<int64_t>(v_base + half * 64 + r) * ldc + u_base + 4 * chunk) = o;
-        }
-    }
-}
-
 template <bool XRC, bool YRC, int EPI, bool TOKEN_V>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_gemm_kernel(GemmArgs g) {
     static_assert(kStages == 4, "the K loop is unrolled over a ring of four buffers");
@@ -477,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dst = static_cast<float*>(g.c0) + ksp * g.c_split_stride;
         }
         store_rows_staged(acc, reinterpret_cast<f32x4_t*>(wave == 0 ? sb0 : wave == 1 ? sb1 : wave == 2 ? sb2 : sb3),
-                          dst, g.ldc, vb + wv * 128, u0 + wu * 128, lane);
+                          dst, g.ldc, vb + wv * 128, u0 + wu * 128, 128, lane);
     } else {
         // kEpiGrad: u = feature f of F, v = permuted row p.  With a1 = a[p][f],
         // a3 = a[p][F + f], gate gv:  h = SiLU(a1) a3, dg += G h,

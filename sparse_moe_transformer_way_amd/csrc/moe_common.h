@@ -87,6 +87,46 @@ __device__ __forceinline__ size_t preact_block(int pb, int fb, int F) {
     return (static_cast<size_t>(pb) * (2 * F / 32) + fb) * 1024;
 }
 
+// Store a wave's 128 x 128 fp32 results acc[bu][bv] (32x32 MFMA C layout:
+// rows v = 32 bv + lane % 32, columns u = 32 bu + 8 (q / 4) + 4 (lane / 32) +
+// q % 4) to dst[v_base + v][u_base + u], for v < rows only, through a 32 KB
+// LDS region stg that no other wave uses.  In the C layout a store instruction would write 32 rows x 32
+// bytes; staged, 64 rows at a time, each store writes 2 rows x 512 contiguous
+// bytes (measured: the scattered stores made the weight-gradient products
+// about a fifth slower).  LDS row r holds 128 floats as 32 chunks of 16 bytes,
+// chunk c at c ^ (r % 32): the 32 rows of a write instruction and the 32
+// chunks of a read hit distinct chunk slots.  LDS runs one wave's
+// instructions in order, so no barrier is needed between the writes and the
+// reads, nor between the two halves.
+__device__ __forceinline__ void store_rows_staged(const f32x16_t (&acc)[4][4], f32x4_t* stg, float* dst,
+                                                  int64_t ldc, int v_base, int u_base, int rows, int lane) {
+    const int fk = lane >> 5;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const int r = b2 * 32 + (lane & 31);  // row within the half
+#pragma unroll
+            for (int bu = 0; bu < 4; ++bu)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x16_t& c = acc[bu][2 * half + b2];
+                    const int chunk = bu * 8 + 2 * q4 + fk;
+                    stg[r * 32 + (chunk ^ (r & 31))] = f32x4_t{c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int r = 2 * i + (lane >> 5);
+            const int chunk = lane & 31;
+            const f32x4_t o = stg[r * 32 + (chunk ^ (r & 31))];
+            if (half * 64 + r < rows)
+                *reinterpret_cast<f32x4_t*>(dst + static_cast<int64_t>(v_base + half * 64 + r) * ldc + u_base +
+                                            4 * chunk) = o;
+        }
+    }
+}
+
 // Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
 constexpr int kMaxExperts = 16;
 constexpr int kMaxTopK = 4;

@@ -714,6 +714,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- epilogue.  32x32 C layout: lane l holds token column l%32 and weight
     // rows 8*(q/4) + 4*(l/32) + q%4 of each block, q = 0..15.
+    if (!DUAL) {
+        // y_perm rows (tokens) of this wave, staged through LDS into row-
+        // contiguous stores once every wave is done with the last block.  Its
+        // padding rows get the (zero or padding-row) sums too: rows of a
+        // segment past the expert's count are unspecified in y_perm.
+        block_barrier<0>();
+        store_rows_staged(acc, reinterpret_cast<f32x4_t*>((wave < 2 ? b0 : b1) + (wave & 1) * (kBufVec / 2)),
+                          static_cast<float*>(out), ld_out, p0 + wave_t * 128, wt * kTW + wave_w * 128,
+                          row_end - (p0 + wave_t * 128), lane);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rt = wave_t * 128 + i * 32 + fr;  // token row within the tile
