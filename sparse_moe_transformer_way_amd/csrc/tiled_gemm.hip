@@ -46,7 +46,11 @@
 //     tile (narrow_tile): 64 or 128 token rows, the weight rows split over the
 //     four waves.
 //   * Padding rows of a token tile copy a real row (gate/up) or the padded rows
-//     of h (down); their outputs are masked in the epilogue.
+//     of h (down).  Gate/up writes zeros for them into h; down writes whatever
+//     they sum to (y_perm rows past an expert's count are unspecified).
+//   * Epilogue stores: gate/up pairs lanes l and l + 32 with a permlane32 swap
+//     so that each lane stores 16 bytes of h; down stages its fp32 rows through
+//     LDS (store_rows_staged) into row-contiguous runs.
 //   * K may be cut into two parts (down projection with few tiles): part s
 //     covers k in [s*K/2, (s+1)*K/2) and writes its own fp32 output buffer.
 #include "moe_common.h"
