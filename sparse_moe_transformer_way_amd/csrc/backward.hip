@@ -18,13 +18,16 @@
 // (nothing of the forward pass is kept), then runs five grouped GEMMs through
 // MFMA kernels, over the expert-grouped rows padded to 256 (the first product
 // reuses the forward pass's tiled gate/up kernel, the others share one kernel):
-//   1. a = [a1 | a3] = xp . [w1; w3]^T       K = d, fp32 (the forward gate/up tiled kernel)
+//   1. a = [a1 | a3] = xp . [w1; w3]^T       K = d, fp32 in 32 x 32 blocks (preact_block;
+//                                             the forward gate/up tiled kernel)
 //   2. G = dyp . w2                           u = F, v = rows, K = d; epilogue
 //      forms h, dg partial sums, da = [da1 | da3] and hg = g h
 //   3. dxp = da . [w1; w3]                    u = d, v = rows, K = 2F
 //   4. dw2_e = hg^T dyp                       u = F, v = d, K = the expert's rows
 //   5. [dw1; dw3]_e = xp^T da                 u = d, v = 2F, K = the expert's rows
 // where xp, dyp are x and dy gathered into permuted rows (zero for padding).
+// Products 3-5 store their fp32 rows through LDS (store_rows_staged); product
+// 2 stores its bf16 outputs 16 bytes per lane after a permlane32 swap.
 //
 // The GEMM computes C[u][v] = sum_k X[u][k] Y[v][k].  Each operand is stored
 // either k-contiguous ([rows][k]) or row-contiguous ([k][rows]); both are
