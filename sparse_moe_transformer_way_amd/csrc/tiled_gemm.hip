@@ -44,7 +44,8 @@
 //     in its L2.
 //   * An expert's last token tile with at most 128 real rows runs as a narrow
 //     tile (narrow_tile): 64 or 128 token rows, the weight rows split over the
-//     four waves.
+//     four waves.  A 64-row narrow tile moves 128 k per buffer (two 64-k
+//     blocks of 40 KB), which is why each buffer is 80 KB.
 //   * Padding rows of a token tile copy a real row (gate/up) or the padded rows
 //     of h (down).  Gate/up writes zeros for them into h; down writes whatever
 //     they sum to (y_perm rows past an expert's count are unspecified).
@@ -69,6 +70,9 @@ constexpr int kBufVec = (kTW + kTT) * kChunks;  // uint4 per buffer (64 KB)
 constexpr int kCopies = 16;                  // copies per lane per block
 constexpr int kGroupVec = 8 * kChunks;       // uint4 of one 8-row copy group (1 KB)
 constexpr int kXcdTiles = 32;                // tiles an XCD runs at once (its CUs)
+// Each of the two LDS buffers: a full tile's block, or two 64-k blocks of a
+// 64-row narrow tile (2 x 40 KB), so the kernel takes all 160 KB of LDS.
+constexpr int kLdsVec = kBufVec > 2 * (kTW + 64) * kChunks ? kBufVec : 2 * (kTW + 64) * kChunks;
 
 typedef void __attribute__((address_space(3)))* lptr_t;
 
@@ -288,50 +292,70 @@ __device__ __forceinline__ void mfma_narrow(const u32x4_t (&f)[2 * (2 + TB)], f3
 }
 
 // 4 * TB MFMAs, each followed by its share of the stage's fragment reads
-// (READ) and of the block's 8 + TB copies (COPY).
-template <int TB, bool READ, bool COPY, int U>
+// (READ) and of NC copies.
+template <int TB, bool READ, int NC, int U>
 __device__ __forceinline__ void sched_narrow_unit() {
     constexpr int kM = 4 * TB;
     constexpr int kR = (U + 1) * 2 * (2 + TB) / kM - U * 2 * (2 + TB) / kM;
-    constexpr int kC = (U + 1) * (8 + TB) / kM - U * (8 + TB) / kM;
+    constexpr int kC = (U + 1) * NC / kM - U * NC / kM;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (READ && kR > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kR, 0);
-    if constexpr (COPY && kC > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kC, 0);
+    if constexpr (kC > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kC, 0);
 }
 
-template <int TB, bool READ, bool COPY, int... U>
+template <int TB, bool READ, int NC, int... U>
 __device__ __forceinline__ void sched_narrow_seq(std::integer_sequence<int, U...>) {
-    (sched_narrow_unit<TB, READ, COPY, U>(), ...);
+    (sched_narrow_unit<TB, READ, NC, U>(), ...);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int TB, bool READ, bool COPY>
+template <int TB, bool READ, int NC>
 __device__ __forceinline__ void sched_narrow() {
-    sched_narrow_seq<TB, READ, COPY>(std::make_integer_sequence<int, 4 * TB>{});
+    sched_narrow_seq<TB, READ, NC>(std::make_integer_sequence<int, 4 * TB>{});
 }
 
-// block_step for a narrow tile (every wave is active).
-template <bool DUAL, int TB, bool COPY, bool NEXT>
+// uint4 of one 64-k block of a narrow tile (weight rows, then its token rows)
+template <int TB>
+constexpr int kNarrowVec = (kTW + 32 * TB) * kChunks;
+
+// block_step for a narrow tile (every wave is active).  A narrow block is SUB
+// consecutive 64-k blocks (SUB = 1 or 2), stored one after the other in the
+// buffer, consumed as 2 * SUB stages of 32 k; the barrier and the next
+// block's copies come before the last stage.  Narrow tiles do a quarter or
+// half of a full tile's MFMAs per block, so with one 64-k block in flight they
+// wait on the copies' latency; SUB = 2 keeps twice the bytes in flight.
+template <bool DUAL, int TB, int SUB, bool COPY, bool NEXT>
 __device__ __forceinline__ void narrow_step(const TileCtx& c, const NarrowCtx& n, uint4* __restrict__ cur,
                                             const uint4* __restrict__ nxt, int kb, u32x4_t (&f0)[2 * (2 + TB)],
                                             u32x4_t (&f1)[2 * (2 + TB)], f32x16_t (&acc)[2][TB]) {
     read_narrow<TB>(n, cur, 1, f1);
     mfma_narrow<TB>(f0, acc);
-    sched_narrow<TB, true, false>();
+    sched_narrow<TB, true, 0>();
+    if constexpr (SUB == 2) {
+        read_narrow<TB>(n, cur + kNarrowVec<TB>, 0, f0);
+        mfma_narrow<TB>(f1, acc);
+        sched_narrow<TB, true, 0>();
+        read_narrow<TB>(n, cur + kNarrowVec<TB>, 1, f1);
+        mfma_narrow<TB>(f0, acc);
+        sched_narrow<TB, true, 0>();
+    }
     if (NEXT) block_barrier<0>();
     if (COPY) {
 #pragma unroll
-        for (int j = 0; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, cur, (kb + 2) * kBK, j);
+        for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+            for (int j = 0; j < 8 + TB; ++j)
+                copy_narrow<DUAL, TB>(c, n, cur + sb * kNarrowVec<TB>, ((kb + 2) * SUB + sb) * kBK, j);
     }
     if (NEXT) read_narrow<TB>(n, nxt, 0, f0);
     mfma_narrow<TB>(f1, acc);
-    sched_narrow<TB, NEXT, COPY>();
+    sched_narrow<TB, NEXT, COPY ? SUB * (8 + TB) : 0>();
 }
 
 // The whole narrow tile: copies, K loop, epilogue.  Gate/up also writes zeros
 // to the segment's rows past the TN token rows (its padding rows), in the
 // tile's 128 columns of h.
-template <bool DUAL, int TB>
+template <bool DUAL, int TB, int SUB>
 __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __restrict__ act,
                                             const int32_t* __restrict__ row_src, void* __restrict__ out,
                                             uint4* b0, uint4* b1, int kpart, int kbase, int ld_act, int ld_out,
@@ -355,9 +379,13 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b0, 0, j);
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b1, kBK, j);
+        for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b0 + sb * kNarrowVec<TB>, sb * kBK, j);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b1 + sb * kNarrowVec<TB>, (SUB + sb) * kBK, j);
 
     NarrowCtx n;
     {
@@ -400,22 +428,26 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[b][i][q] = 0.0f;
 
-    const int nb = kpart / kBK;  // a multiple of 4, >= 4
+    const int nb = kpart / (SUB * kBK);  // even and >= 4 (the caller picks SUB so)
 #pragma unroll
-    for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b0, 0, j);
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-    for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b1, kBK, j);
-    block_barrier<TB>();  // block 0 has landed (block 1's token copies may not have)
+        for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b0 + sb * kNarrowVec<TB>, sb * kBK, j);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int j = 8; j < 8 + TB; ++j) copy_narrow<DUAL, TB>(c, n, b1 + sb * kNarrowVec<TB>, (SUB + sb) * kBK, j);
+    block_barrier<SUB * TB>();  // block 0 has landed (block 1's token copies may not have)
     u32x4_t f0[2 * (2 + TB)], f1[2 * (2 + TB)];
     read_narrow<TB>(n, b0, 0, f0);
     int kb = 0;
     do {
-        narrow_step<DUAL, TB, true, true>(c, n, b0, b1, kb, f0, f1, acc);
-        narrow_step<DUAL, TB, true, true>(c, n, b1, b0, kb + 1, f0, f1, acc);
+        narrow_step<DUAL, TB, SUB, true, true>(c, n, b0, b1, kb, f0, f1, acc);
+        narrow_step<DUAL, TB, SUB, true, true>(c, n, b1, b0, kb + 1, f0, f1, acc);
         kb += 2;
     } while (kb < nb - 2);
-    narrow_step<DUAL, TB, false, true>(c, n, b0, b1, kb, f0, f1, acc);
-    narrow_step<DUAL, TB, false, false>(c, n, b1, b0, kb + 1, f0, f1, acc);
+    narrow_step<DUAL, TB, SUB, false, true>(c, n, b0, b1, kb, f0, f1, acc);
+    narrow_step<DUAL, TB, SUB, false, false>(c, n, b1, b0, kb + 1, f0, f1, acc);
 
     // epilogue (32x32 C layout as in the full tile)
 #pragma unroll
@@ -593,8 +625,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_wt,
     int ld_out, int n_src, int P, int ksplit, size_t split_stride, int n_exp, int topk, int tail_rows) {
-    __shared__ uint4 b0[kBufVec];
-    __shared__ uint4 b1[kBufVec];
+    __shared__ uint4 b0[kLdsVec];
+    __shared__ uint4 b1[kLdsVec];
 
     // ---- tile of this workgroup (the grid covers the worst case; spare
     // workgroups exit here)
@@ -644,12 +676,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 
     if (!PREACT && valid <= 128) {
-        if (valid <= 64)
-            narrow_tile<DUAL, 2>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
-                                 valid, row_end);
+        // K parts are multiples of 256: kpart / 128 is even, and at least 4 from 512 on
+        if (valid <= 64 && kpart >= 512)
+            narrow_tile<DUAL, 2, 2>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt,
+                                    p0, valid, row_end);
+        else if (valid <= 64)
+            narrow_tile<DUAL, 2, 1>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt,
+                                    p0, valid, row_end);
         else
-            narrow_tile<DUAL, 4>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt, p0,
-                                 valid, row_end);
+            narrow_tile<DUAL, 4, 1>(c, act, row_src, out, b0, b1, kpart, kbase, ld_act, ld_out, n_src, topk, wt,
+                                    p0, valid, row_end);
         return;
     }
 
