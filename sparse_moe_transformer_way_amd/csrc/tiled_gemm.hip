@@ -118,6 +118,7 @@ struct TileCtx {
     int dma;                      // uint4 offset of this wave's first copy group in a buffer
     int rd[4];                    // per (half of the block, k16 half): fragment index in weight block 0
     int rdt;                      // uint4 distance from weight block 0 to token block 0
+    uint32_t pfo;                 // down: lane byte offset of its prefetch, weight row `lane`
 };
 
 // Weight block j of this wave (uint4 offset from block 0).  Gate/up: blocks 0,
@@ -184,6 +185,15 @@ __device__ __forceinline__ void sched_half() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Down projection: at the end of block kb each wave also loads one dword from
+// each of its 64 w2 rows in block kb + 3 (a 128-byte line per row), which
+// brings that block's weight lines into L2 a block before they are copied.
+// w2 and h do not fit the MALL together, so the down projection's copies wait
+// on HBM; gate/up (its gathered x fits the MALL) gains nothing from it.
+constexpr int kPrefetchAhead = 3;
+template <bool DUAL>
+constexpr bool kPrefetch = !DUAL;
+
 // Block kb (in `cur`) as two 32-k stages.  On entry its first half's fragments
 // are in f0 and, for every wave, the block is complete in `cur`.
 //   first half : read the second half's fragments into f1; MFMAs on f0.
@@ -191,17 +201,26 @@ __device__ __forceinline__ void sched_half() {
 //                and every wave has read all of `cur` - then (COPY) copy block
 //                kb+2 into `cur` and read block kb+1's first half into f0 from
 //                `nxt`; MFMAs on f1.
-// The barrier waits for every outstanding copy (vmcnt 0): the only ones are
-// block kb+1's, issued a block earlier.
-template <bool DUAL, bool ACTIVE, bool COPY, bool NEXT>
+//   then       : (PF, down only) the prefetch of block kb + 3 into pf, after a
+//                scheduling fence, so it is the wave's last memory operation.
+// The barrier waits for block kb+1's copies, issued a block earlier: for every
+// outstanding vector-memory operation (vmcnt 0), or (PFWAIT) for all but the
+// last one, the prefetch issued after those copies.  A prefetch's register is
+// written two blocks after its load (the load of block kb - 2 has completed by
+// block kb's barrier); CONSUME marks it as read there, so the compiler keeps
+// the load and never has to wait for it.
+template <bool DUAL, bool ACTIVE, bool COPY, bool NEXT, bool PFWAIT = false, bool CONSUME = false, bool PF = false>
 __device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__ cur, const uint4* __restrict__ nxt,
-                                           int kb, Frag16& f0, Frag16& f1, f32x16_t (&acc)[4][4]) {
+                                           int kb, int nb, Frag16& f0, Frag16& f1, f32x16_t (&acc)[4][4],
+                                           uint32_t& pf) {
+    constexpr bool kPf = kPrefetch<DUAL>;
     if (ACTIVE) {
         read_half<DUAL>(c, cur, 1, f1);
         mfma_half(f0, acc);
         sched_half<true, false>();
     }
-    if (NEXT) block_barrier<0>();
+    if (NEXT) block_barrier<(kPf && PFWAIT) ? 1 : 0>();
+    if (kPf && CONSUME) asm volatile("" ::"v"(pf));
     if (COPY) {
 #pragma unroll
         for (int j = 0; j < kCopies; ++j) copy_one<DUAL>(c, cur, (kb + 2) * kBK, j);
@@ -211,24 +230,34 @@ __device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__
         mfma_half(f1, acc);
         sched_half<NEXT, COPY>();
     }
+    if (kPf && PF) {
+        __builtin_amdgcn_sched_barrier(0);
+        pf = __builtin_amdgcn_raw_buffer_load_b32(c.wres, c.pfo, 2 * min(kb + kPrefetchAhead, nb - 1) * kBK, 0);
+    }
 }
 
 // The K loop over nb blocks (nb a multiple of 4, >= 4).  Before it: blocks 0
 // and 1 are being copied into b0 and b1, the weights of both first, then the
-// tokens of block 0, then those of block 1.
+// tokens of block 0, then those of block 1.  Blocks 0 and 1 are peeled: no
+// prefetch is outstanding at block 0's barrier, and none is consumed before
+// block 2.
 template <bool DUAL, bool ACTIVE>
 __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1, int nb, f32x16_t (&acc)[4][4]) {
     block_barrier<kCopies / 2>();  // block 0 has landed (block 1's token copies may not have)
     Frag16 f0, f1;
+    uint32_t pf0 = 0, pf1 = 0;  // prefetch registers of the even and the odd blocks
     if (ACTIVE) read_half<DUAL>(c, b0, 0, f0);
-    int kb = 0;
-    do {
-        block_step<DUAL, ACTIVE, true, true>(c, b0, b1, kb, f0, f1, acc);
-        block_step<DUAL, ACTIVE, true, true>(c, b1, b0, kb + 1, f0, f1, acc);
+    block_step<DUAL, ACTIVE, true, true, false, false, true>(c, b0, b1, 0, nb, f0, f1, acc, pf0);
+    block_step<DUAL, ACTIVE, true, true, true, false, true>(c, b1, b0, 1, nb, f0, f1, acc, pf1);
+    int kb = 2;
+    while (kb < nb - 2) {
+        block_step<DUAL, ACTIVE, true, true, true, true, true>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
+        block_step<DUAL, ACTIVE, true, true, true, true, true>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
         kb += 2;
-    } while (kb < nb - 2);
-    block_step<DUAL, ACTIVE, false, true>(c, b0, b1, kb, f0, f1, acc);
-    block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, f0, f1, acc);
+    }
+    block_step<DUAL, ACTIVE, false, true, true, true, false>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
+    block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
+    if (kPrefetch<DUAL>) asm volatile("" ::"v"(pf1));
 }
 
 // ---- Narrow tiles.  An expert's last token tile often holds few real rows
@@ -673,6 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         c.wo[1] = (static_cast<uint32_t>(rl) * Kdim + 8u * ch1) * 2u;
         c.wstride = 8 * Kdim * 2;
         c.dma = wave * 64 * kChunks;
+        c.pfo = static_cast<uint32_t>(lane) * Kdim * 2u;
     }
 
     if (!PREACT && valid <= 128) {
