@@ -34,6 +34,71 @@ __device__ __forceinline__ bool before(float v, int i, float w, int j) {
     return j < 0 || v > w || (v == w && i < j);
 }
 
+// The lane's dot products over chunks cb, cb + 64, ... of [cbeg, cend) for
+// TOK tokens (rows past T read row T - 1; their sums are never used).  U
+// chunks per pass, all of their loads issued before any multiply-add: at
+// d = 4096 a decode block's lanes cover two chunks each, and one pass then
+// costs one memory round trip instead of two.  FULL: W_g rows are NE floats
+// (vector loads); otherwise n floats, padded with zeros.
+template <bool BF16, int TOK, int NE, bool FULL>
+__device__ __forceinline__ void chunk_dots(const void* __restrict__ xv, const float* __restrict__ wg, int T, int d,
+                                           int n, int t0, int cbeg, int cend, int lane, float (&acc)[TOK][NE]) {
+    constexpr int U = (TOK == 1 && NE == 8) ? 2 : 1;
+    for (int cb = cbeg + lane; cb < cend; cb += 64 * U) {
+        float w[U][8][NE];
+        float xf[U][TOK][8];
+        bool in[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ch = cb + 64 * u;
+            in[u] = ch < cend;  // a chunk past the wave's range is loaded in range, then zeroed
+            const int k0 = (in[u] ? ch : cbeg) * 8;
+            if (FULL) {
+                const float4* wp = reinterpret_cast<const float4*>(wg + static_cast<size_t>(k0) * NE);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int q = 0; q < NE / 4; ++q) {
+                        const float4 a = wp[j * (NE / 4) + q];
+                        w[u][j][4 * q] = a.x; w[u][j][4 * q + 1] = a.y; w[u][j][4 * q + 2] = a.z; w[u][j][4 * q + 3] = a.w;
+                    }
+            } else {
+                const float* wr = wg + static_cast<size_t>(k0) * n;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) w[u][j][e] = e < n ? wr[j * n + e] : 0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < TOK; ++t) {
+                const int tok = min(t0 + t, T - 1);
+                if (BF16) {
+                    const bf16_t* xr = static_cast<const bf16_t*>(xv) + static_cast<size_t>(tok) * d + k0;
+                    unpack_bf16x8(*reinterpret_cast<const uint4*>(xr), xf[u][t]);
+                } else {
+                    const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(tok) * d + k0;
+                    const float4 a = reinterpret_cast<const float4*>(xr)[0];
+                    const float4 b = reinterpret_cast<const float4*>(xr)[1];
+                    xf[u][t][0] = a.x; xf[u][t][1] = a.y; xf[u][t][2] = a.z; xf[u][t][3] = a.w;
+                    xf[u][t][4] = b.x; xf[u][t][5] = b.y; xf[u][t][6] = b.z; xf[u][t][7] = b.w;
+                }
+            }
+        }
+        // An unused chunk adds 0 * 0 (selected, not branched around: a branch
+        // lets the compiler sink that chunk's loads behind the first one's
+        // multiply-adds, a second round trip).
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < TOK; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int e = 0; e < NE; ++e)
+                        acc[t][e] = fmaf(in[u] ? xf[u][t][j] : 0.0f, in[u] ? w[u][j][e] : 0.0f, acc[t][e]);
+    }
+}
+
 // TOK tokens per block, NE = expert slots (n <= NE experts are real).
 template <bool BF16, int TOK, int NE>
 __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict__ xv,
@@ -48,54 +113,16 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
     const int nch = d >> 3;
     const int cbeg = wave * nch / kWaves;
     const int cend = (wave + 1) * nch / kWaves;
-    const bool full = n == NE;  // W_g rows are NE floats: vector loads
 
     float acc[TOK][NE];
 #pragma unroll
     for (int t = 0; t < TOK; ++t)
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[t][e] = 0.0f;
-
-    for (int ch = cbeg + lane; ch < cend; ch += 64) {
-        const int k0 = ch * 8;
-        float w[8][NE];
-        if (full) {
-            const float4* wp = reinterpret_cast<const float4*>(wg + static_cast<size_t>(k0) * NE);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int q = 0; q < NE / 4; ++q) {
-                    const float4 a = wp[j * (NE / 4) + q];
-                    w[j][4 * q] = a.x; w[j][4 * q + 1] = a.y; w[j][4 * q + 2] = a.z; w[j][4 * q + 3] = a.w;
-                }
-        } else {
-            const float* wr = wg + static_cast<size_t>(k0) * n;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < NE; ++e) w[j][e] = e < n ? wr[j * n + e] : 0.0f;
-        }
-#pragma unroll
-        for (int t = 0; t < TOK; ++t) {
-            if (t0 + t < T) {
-                float xf[8];
-                if (BF16) {
-                    const bf16_t* xr = static_cast<const bf16_t*>(xv) + static_cast<size_t>(t0 + t) * d + k0;
-                    unpack_bf16x8(*reinterpret_cast<const uint4*>(xr), xf);
-                } else {
-                    const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t0 + t) * d + k0;
-                    const float4 a = reinterpret_cast<const float4*>(xr)[0];
-                    const float4 b = reinterpret_cast<const float4*>(xr)[1];
-                    xf[0] = a.x; xf[1] = a.y; xf[2] = a.z; xf[3] = a.w;
-                    xf[4] = b.x; xf[5] = b.y; xf[6] = b.z; xf[7] = b.w;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-#pragma unroll
-                    for (int e = 0; e < NE; ++e) acc[t][e] = fmaf(xf[j], w[j][e], acc[t][e]);
-            }
-        }
-    }
+    if (n == NE)
+        chunk_dots<BF16, TOK, NE, true>(xv, wg, T, d, n, t0, cbeg, cend, lane, acc);
+    else
+        chunk_dots<BF16, TOK, NE, false>(xv, wg, T, d, n, t0, cbeg, cend, lane, acc);
 
 #pragma unroll
     for (int t = 0; t < TOK; ++t)
