@@ -15,56 +15,93 @@ namespace moe {
 
 namespace {
 
-template <bool BF16, int K>
+// One 4-column group c of token t's output from its loaded slot values a[s]
+// (the two K-parts already added; dropped slots are zero) and the residual.
+template <bool BF16, int K, bool RES>
+__device__ __forceinline__ void combine_store(const float4 (&a)[K], const float (&g)[K], const void* __restrict__ residual,
+                                              void* y, size_t o) {
+    float v[4] = {g[0] * a[0].x, g[0] * a[0].y, g[0] * a[0].z, g[0] * a[0].w};
+#pragma unroll
+    for (int s = 1; s < K; ++s) {
+        v[0] += g[s] * a[s].x; v[1] += g[s] * a[s].y; v[2] += g[s] * a[s].z; v[3] += g[s] * a[s].w;
+    }
+    if (BF16) {
+        if constexpr (RES) {
+            const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(residual) + o);
+            v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xffff0000u);
+            v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xffff0000u);
+        }
+        uint2 out;
+        out.x = pack_bf16x2(v[0], v[1]);
+        out.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(y) + o) = out;
+    } else {
+        if constexpr (RES) {
+            const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) + o);
+            v[0] += r.x; v[1] += r.y; v[2] += r.z; v[3] += r.w;
+        }
+        *reinterpret_cast<float4*>(static_cast<float*>(y) + o) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Slot s of group c: y_perm row r[s] (+ its second K-part), zero for a dropped
+// slot (r < 0 reads row 0 and discards it).
+template <int K, bool HI>
+__device__ __forceinline__ void combine_load(const float4* const (&p)[K], const float4* const (&q)[K],
+                                             const uint32_t (&keep)[K], int c, float4 (&a)[K]) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        float4 v = p[s][c];
+        if constexpr (HI) {
+            const float4 v2 = q[s][c];
+            v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+        }
+        // a bit mask, not a select: the compiler turns a select on a uniform
+        // flag into a branch and sinks the loads into it
+        a[s] = make_float4(__uint_as_float(__float_as_uint(v.x) & keep[s]), __uint_as_float(__float_as_uint(v.y) & keep[s]),
+                           __uint_as_float(__float_as_uint(v.z) & keep[s]), __uint_as_float(__float_as_uint(v.w) & keep[s]));
+    }
+}
+
+// One block of 256 threads per token.  Full passes take U groups per thread
+// with every load issued before the first store (a decode row, d = 4096, is
+// one pass), then a plain loop takes what is left.  HI: y_perm has a second
+// K-part to add; RES: a residual is added.
+template <bool BF16, int K, bool HI, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ residual, void* y,
                                                       int d, const float* __restrict__ y_perm_hi) {
+    constexpr int U = 4;
     const int t = blockIdx.x;
-    int r[K];
     float g[K];
+    uint32_t keep[K];  // all ones for a kept slot, zero for a dropped one
     const float4* p[K];
+    const float4* q[K];
 #pragma unroll
     for (int s = 0; s < K; ++s) {
-        r[s] = row_of[K * t + s];
+        const int r = row_of[K * t + s];
         g[s] = gate[K * t + s];
-        p[s] = reinterpret_cast<const float4*>(y_perm + static_cast<size_t>(r[s] < 0 ? 0 : r[s]) * d);
+        keep[s] = r >= 0 ? 0xffffffffu : 0u;
+        const size_t row = static_cast<size_t>(r < 0 ? 0 : r) * d;
+        p[s] = reinterpret_cast<const float4*>(y_perm + row);
+        q[s] = reinterpret_cast<const float4*>((HI ? y_perm_hi : y_perm) + row);
     }
-    for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+    const int n4 = d / 4;
+    int c = threadIdx.x;
+    for (; c + (U - 1) * 256 < n4; c += U * 256) {
+        float4 a[U][K];
 #pragma unroll
-        for (int s = 0; s < K; ++s) {
-            if (r[s] < 0) continue;
-            float4 a = p[s][c];
-            if (y_perm_hi != nullptr) {
-                const float4 a2 = reinterpret_cast<const float4*>(y_perm_hi + static_cast<size_t>(r[s]) * d)[c];
-                a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-            }
-            if (s == 0) {
-                v[0] = g[s] * a.x; v[1] = g[s] * a.y; v[2] = g[s] * a.z; v[3] = g[s] * a.w;
-            } else {
-                v[0] += g[s] * a.x; v[1] += g[s] * a.y; v[2] += g[s] * a.z; v[3] += g[s] * a.w;
-            }
-        }
-        const size_t o = static_cast<size_t>(t) * d + 4 * c;
-        if (BF16) {
-            if (residual != nullptr) {
-                const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(residual) + o);
-                v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xffff0000u);
-                v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xffff0000u);
-            }
-            uint2 out;
-            out.x = pack_bf16x2(v[0], v[1]);
-            out.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(y) + o) = out;
-        } else {
-            if (residual != nullptr) {
-                const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) + o);
-                v[0] += r.x; v[1] += r.y; v[2] += r.z; v[3] += r.w;
-            }
-            *reinterpret_cast<float4*>(static_cast<float*>(y) + o) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+        for (int u = 0; u < U; ++u) combine_load<K, HI>(p, q, keep, c + 256 * u, a[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            combine_store<BF16, K, RES>(a[u], g, residual, y, static_cast<size_t>(t) * d + 4 * (c + 256 * u));
+    }
+    for (; c < n4; c += 256) {
+        float4 a[K];
+        combine_load<K, HI>(p, q, keep, c, a);
+        combine_store<BF16, K, RES>(a, g, residual, y, static_cast<size_t>(t) * d + 4 * c);
     }
 }
 
@@ -115,15 +152,25 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
 
 }  // namespace
 
-template <bool BF16>
+template <bool BF16, bool HI, bool RES>
 static void combine_k(const Shape& s, const float* y_perm, const int32_t* row_of, const float* gate,
                       const void* residual, void* y, hipStream_t st, const float* y_perm_hi) {
     switch (s.K) {
-        case 1: combine_kernel<BF16, 1><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        case 2: combine_kernel<BF16, 2><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        case 3: combine_kernel<BF16, 3><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        default: combine_kernel<BF16, 4><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 1: combine_kernel<BF16, 1, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 2: combine_kernel<BF16, 2, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 3: combine_kernel<BF16, 3, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        default: combine_kernel<BF16, 4, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
     }
+}
+
+template <bool BF16>
+static void combine_dispatch(const Shape& s, const float* y_perm, const int32_t* row_of, const float* gate,
+                             const void* residual, void* y, hipStream_t st, const float* y_perm_hi) {
+    const bool hi = y_perm_hi != nullptr, res = residual != nullptr;
+    if (hi && res) combine_k<BF16, true, true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+    else if (hi) combine_k<BF16, true, false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+    else if (res) combine_k<BF16, false, true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+    else combine_k<BF16, false, false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
 }
 
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
@@ -132,9 +179,9 @@ hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* ro
     static_assert(kMaxTopK == 4, "one combine instance per K");
     if (s.K < 1 || s.K > kMaxTopK) return hipErrorInvalidValue;
     if (s.bf16)
-        combine_k<true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+        combine_dispatch<true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
     else
-        combine_k<false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+        combine_dispatch<false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
     return hipGetLastError();
 }
 
