@@ -229,11 +229,16 @@ def expert_rows(x, row_src, offsets, w1, w3, w2, K: int = 2):
 
 def combine(y_perm, row_of, gates, residual=None):
     """y[t] = sum_s gates[t,s] * y_perm[row_of[t,s]] (+ residual[t]), fp32,
-    slots summed in slot order."""
+    slots summed in slot order.  A slot whose row is negative (an assignment
+    to no expert, dropped by the grouping) adds nothing."""
     T, K = row_of.shape
     y = np.zeros((T, y_perm.shape[1]), dtype=F32)
+    yp = np.asarray(y_perm, F32)
     for s in range(K):
-        y += np.asarray(gates[:, s:s + 1], F32) * np.asarray(y_perm, F32)[row_of[:, s]]
+        r = np.asarray(row_of[:, s])
+        keep = r >= 0
+        term = np.asarray(gates[:, s:s + 1], F32) * yp[np.where(keep, r, 0)]
+        y += np.where(keep[:, None], term, F32(0))
     if residual is not None:
         y += np.asarray(residual, F32)
     return y

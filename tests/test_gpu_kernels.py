@@ -245,21 +245,28 @@ def test_grouped_swiglu_empty_and_full_experts():
 # Combine and RMSNorm
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,T,d,residual", [("f32", 64, 128, False), ("bf16", 333, 4096, False),
-                                                ("bf16", 333, 512, True), ("f32", 7, 64, True)])
-def test_combine(dtype, T, d, residual):
+# d = 4608: one full pass of four column groups per thread, then a remainder;
+# `drop`: some slots have no row (an assignment to no expert).
+@pytest.mark.parametrize("dtype,T,d,residual,drop", [("f32", 64, 128, False, False), ("bf16", 333, 4096, False, False),
+                                                     ("bf16", 333, 512, True, False), ("f32", 7, 64, True, False),
+                                                     ("bf16", 97, 4608, True, True), ("f32", 40, 4608, False, True)])
+def test_combine(dtype, T, d, residual, drop):
     rng = np.random.default_rng(T + d)
     idx = _random_idx(T, T)
     grp = oracle.group_by_expert(idx, 8, 16)
+    row_of = grp["row_of"].copy()
+    if drop:
+        row_of[rng.random(row_of.shape) < 0.2] = -1
+        row_of[0] = -1  # one token with no expert at all
     P = len(grp["row_src"])
     yp = rng.standard_normal((P, d)).astype(np.float32)
     g0 = rng.uniform(0.5, 1.0, T).astype(np.float32)
     gates = np.stack([g0, (1 - g0)], axis=1).astype(np.float32)
     res = torch.randn(T, d).to(DT[dtype]) if residual else None
     desc = moe.make_desc(d, 512, dtype=DT[dtype])
-    y = moe.moe_combine(desc, torch.from_numpy(yp).cuda(), torch.from_numpy(grp["row_of"]).cuda(),
+    y = moe.moe_combine(desc, torch.from_numpy(yp).cuda(), torch.from_numpy(row_of).cuda(),
                         torch.from_numpy(gates).cuda(), residual=None if res is None else res.cuda())
-    ref = oracle.combine(yp, grp["row_of"], gates, None if res is None else res.float().numpy())
+    ref = oracle.combine(yp, row_of, gates, None if res is None else res.float().numpy())
     got = y.float().cpu().numpy()
     if dtype == "bf16":
         ref = oracle.round_bf16(ref)

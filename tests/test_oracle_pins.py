@@ -315,6 +315,27 @@ def test_sparse_path_equals_dense():
     np.testing.assert_allclose(y, out["y"], rtol=1e-5, atol=1e-6)
 
 
+def test_combine_dropped_slots_brute_force():
+    """A slot whose permuted row is negative adds nothing (an assignment to no
+    expert is dropped by the grouping); a token with every slot dropped keeps
+    only its residual.  Element-by-element loops on a tiny case."""
+    rng = np.random.default_rng(3)
+    T, K, d, P = 5, 2, 3, 7
+    y_perm = rng.standard_normal((P, d)).astype(np.float32)
+    row_of = np.array([[0, 1], [-1, 2], [3, -1], [-1, -1], [6, 5]], np.int32)
+    gates = rng.uniform(0.1, 1.0, (T, K)).astype(np.float32)
+    res = rng.standard_normal((T, d)).astype(np.float32)
+    got = oracle.combine(y_perm, row_of, gates, res)
+    for t in range(T):
+        for j in range(d):
+            acc = 0.0
+            for s in range(K):
+                if row_of[t, s] >= 0:
+                    acc += float(gates[t, s]) * float(y_perm[row_of[t, s], j])
+            assert abs(got[t, j] - (acc + float(res[t, j]))) <= 1e-5 * (1.0 + abs(acc))
+    np.testing.assert_array_equal(got[3], res[3])
+
+
 @pytest.mark.parametrize("n,K", [(6, 3), (16, 4), (4, 1)])
 def test_sparse_path_equals_dense_general_k(n, K):
     """Grouped rows + slot-order combine reproduce the dense per-token sum for
