@@ -31,9 +31,12 @@ def layer(T, d, F, dtype, seed=0, workload=200):
 # Router
 # ---------------------------------------------------------------------------
 
-# T <= 256 runs one token per block, larger T eight: 256 and 257 straddle the switch
+# T <= 256 runs one token per block, larger T eight: 256 and 257 straddle the switch.
+# With one token per block a lane takes two 8-channel chunks per pass: d = 4096
+# fills both, 1536 only the first, 4608 a full pass and then a half-empty one.
 @pytest.mark.parametrize("dtype,T,d", [("f32", 64, 128), ("bf16", 37, 512), ("bf16", 1, 4096),
-                                       ("bf16", 256, 512), ("bf16", 257, 512),
+                                       ("bf16", 32, 4096), ("bf16", 19, 1536), ("bf16", 32, 4608),
+                                       ("f32", 5, 4608), ("bf16", 256, 512), ("bf16", 257, 512),
                                        ("bf16", 1000, 512), ("f32", 17, 8)])
 def test_router(dtype, T, d):
     inp = layer(T, d, 512, dtype, seed=T)
