@@ -592,42 +592,85 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(const int32_t* __restri
 
 // dx[t] = sum_s (dxp + dxp_hi)[row_of[t, s]] (slot order) + sum_s dl[t, e_s] W_g[:, e_s], one
 // rounding to bf16; dxp and dxp_hi are the w1 and w3 parts of the per-row input gradients.
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const float* __restrict__ dxp_hi,
+template <int K>
+__device__ __forceinline__ void bwd_dx_group(const float4* const (&pa)[K], const float4* const (&pb)[K],
+                                             const int (&es)[K], const float* __restrict__ wg, int n, int c,
+                                             float4 (&x)[K], float4 (&y)[K], float (&w)[K][4]) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        x[s] = pa[s][c];
+        y[s] = pb[s][c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[s][i] = wg[static_cast<int64_t>(4 * c + i) * n + es[s]];
+    }
+}
+
+// The w1 and w3 parts of each slot, in slot order; a slot with no row is
+// cleared by a bit mask (a select on the uniform flag becomes a branch that the
+// loads sink into).  Then the router term and one rounding.
+template <int K>
+__device__ __forceinline__ void bwd_dx_store(const float4 (&x)[K], const float4 (&y)[K], const float (&w)[K][4],
+                                             const uint32_t (&keep)[K], const float (&ls)[K],
+                                             bf16_t* __restrict__ out) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        v[0] += __uint_as_float(__float_as_uint(x[s].x + y[s].x) & keep[s]);
+        v[1] += __uint_as_float(__float_as_uint(x[s].y + y[s].y) & keep[s]);
+        v[2] += __uint_as_float(__float_as_uint(x[s].z + y[s].z) & keep[s]);
+        v[3] += __uint_as_float(__float_as_uint(x[s].w + y[s].w) & keep[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < K; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fmaf(ls[s], w[s][i], v[i]);
+    uint2 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(out) = o;
+}
+
+// One block of 256 threads per token; full passes take U column groups per
+// thread with every load issued before the first store, then a plain loop.
+template <int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void bwd_dx_kernel(const float* __restrict__ dxp, const float* __restrict__ dxp_hi,
                                                      const int32_t* __restrict__ row_of,
                                                      const int32_t* __restrict__ idx, const float* __restrict__ dl,
-                                                     const float* __restrict__ wg, int d, int n, int K,
+                                                     const float* __restrict__ wg, int d, int n,
                                                      bf16_t* __restrict__ dx) {
+    constexpr int U = 4;
     const int t = blockIdx.x;
-    int p[kMaxTopK], es[kMaxTopK];
-    float ls[kMaxTopK];
+    int es[K];
+    float ls[K];
+    uint32_t keep[K];
+    const float4* pa[K];
+    const float4* pb[K];
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        p[s] = s < K ? row_of[t * K + s] : -1;
-        es[s] = s < K ? idx[t * K + s] : 0;
-        ls[s] = s < K ? dl[static_cast<int64_t>(t) * n + es[s]] : 0.0f;
+    for (int s = 0; s < K; ++s) {
+        const int p = row_of[t * K + s];
+        es[s] = idx[t * K + s];
+        ls[s] = dl[static_cast<int64_t>(t) * n + es[s]];
+        keep[s] = p >= 0 ? 0xffffffffu : 0u;
+        const int64_t row = static_cast<int64_t>(p < 0 ? 0 : p) * d;
+        pa[s] = reinterpret_cast<const float4*>(dxp + row);
+        pb[s] = reinterpret_cast<const float4*>(dxp_hi + row);
     }
-    for (int c = threadIdx.x; c < d / 4; c += 256) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16_t* out = dx + static_cast<int64_t>(t) * d;
+    const int n4 = d / 4;
+    int c = threadIdx.x;
+    for (; c + (U - 1) * 256 < n4; c += U * 256) {
+        float4 x[U][K], y[U][K];
+        float w[U][K][4];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (s < K && p[s] >= 0) {
-                float4 a = reinterpret_cast<const float4*>(dxp + static_cast<int64_t>(p[s]) * d)[c];
-                const float4 b = reinterpret_cast<const float4*>(dxp_hi + static_cast<int64_t>(p[s]) * d)[c];
-                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;  // the w1 and w3 parts
-                v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-            }
-        }
+        for (int u = 0; u < U; ++u) bwd_dx_group<K>(pa, pb, es, wg, n, c + 256 * u, x[u], y[u], w[u]);
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (s < K) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = fmaf(ls[s], wg[static_cast<int64_t>(4 * c + i) * n + es[s]], v[i]);
-            }
-        }
-        uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(dx + static_cast<int64_t>(t) * d + 4 * c) = o;
+        for (int u = 0; u < U; ++u) bwd_dx_store<K>(x[u], y[u], w[u], keep, ls, out + 4 * (c + 256 * u));
+    }
+    for (; c < n4; c += 256) {
+        float4 x[K], y[K];
+        float w[K][4];
+        bwd_dx_group<K>(pa, pb, es, wg, n, c, x, y, w);
+        bwd_dx_store<K>(x, y, w, keep, ls, out + 4 * c);
     }
 }
 
@@ -805,7 +848,16 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     // router gradient, dx, dW_g
     bwd_router_kernel<<<(T + 255) / 256, 256, 0, st>>>(w.idx, w.gate, w.row_of, w.dgp, F / kTU, P, T, n, K, w.dl);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    bwd_dx_kernel<<<T, 256, 0, st>>>(w.dxp, w.dxp + static_cast<int64_t>(P) * d, w.row_of, w.idx, w.dl, wg, d, n, K, static_cast<bf16_t*>(dx));
+    {
+        const float* hi = w.dxp + static_cast<int64_t>(P) * d;
+        bf16_t* dxo = static_cast<bf16_t*>(dx);
+        switch (K) {
+            case 1: bwd_dx_kernel<1><<<T, 256, 0, st>>>(w.dxp, hi, w.row_of, w.idx, w.dl, wg, d, n, dxo); break;
+            case 2: bwd_dx_kernel<2><<<T, 256, 0, st>>>(w.dxp, hi, w.row_of, w.idx, w.dl, wg, d, n, dxo); break;
+            case 3: bwd_dx_kernel<3><<<T, 256, 0, st>>>(w.dxp, hi, w.row_of, w.idx, w.dl, wg, d, n, dxo); break;
+            default: bwd_dx_kernel<4><<<T, 256, 0, st>>>(w.dxp, hi, w.row_of, w.idx, w.dl, wg, d, n, dxo); break;
+        }
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int chunks = (T + kDwgTokens - 1) / kDwgTokens;
     bwd_dwg_partial_kernel<<<dim3((d + 255) / 256, chunks), 256, 0, st>>>(xb, w.dl, T, d, n, w.dwg_part);
