@@ -124,21 +124,34 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const void* __restrict
     else
         chunk_dots<BF16, TOK, NE, false>(xv, wg, T, d, n, t0, cbeg, cend, lane, acc);
 
+    // Wave sums of the V = TOK * NE partial sums by recursive halving: at the
+    // step with lane offset o, a lane keeps half of its remaining values (the
+    // upper half if its lane bit o is set), sends the other half to lane ^ o
+    // and adds what it receives.  After log2 V steps lane L holds value
+    // L >> (6 - log2 V) summed over the V lanes that share its low bits; a
+    // butterfly over those bits completes the sum.  63 exchanges for 64
+    // values, against 384 for a butterfly per value.
+    constexpr int V = TOK * NE;
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "a power of two up to 64 values");
+    float vals[V];
 #pragma unroll
     for (int t = 0; t < TOK; ++t)
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            float v = acc[t][e];
+        for (int e = 0; e < NE; ++e) vals[t * NE + e] = acc[t][e];
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-            acc[t][e] = v;
+    for (int half = V / 2, off = 32; half >= 1; half >>= 1, off >>= 1) {
+        const bool upper = (lane & off) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = upper ? vals[i] : vals[i + half];
+            const float keep = upper ? vals[i + half] : vals[i];
+            vals[i] = keep + __shfl_xor(send, off, 64);
         }
-    if (lane == 0) {
-#pragma unroll
-        for (int t = 0; t < TOK; ++t)
-#pragma unroll
-            for (int e = 0; e < NE; ++e) part[wave][t][e] = acc[t][e];
     }
+    constexpr int kLow = 64 / V;  // lanes that hold parts of the same value
+#pragma unroll
+    for (int off = kLow / 2; off >= 1; off >>= 1) vals[0] += __shfl_xor(vals[0], off, 64);
+    if ((lane & (kLow - 1)) == 0) (&part[wave][0][0])[lane / kLow] = vals[0];
     __syncthreads();
     if (wave != 0 || lane >= TOK) return;
     const int t = lane;
