@@ -561,13 +561,17 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(const bf16_t* __restric
 }
 
 // dl[t, :]: zero except the K selected experts, dl_s = g_s (dg_s - sum_j g_j dg_j),
-// dg_s = the sum of the row's partials over the nut feature tiles, in tile order.
+// dg_s = the sum of the row's partials over the nut feature tiles (lane-strided
+// sums, then a butterfly: a fixed order).
 __global__ __launch_bounds__(256) void bwd_router_kernel(const int32_t* __restrict__ idx,
                                                          const float* __restrict__ gate,
                                                          const int32_t* __restrict__ row_of,
                                                          const float* __restrict__ dgp, int nut, int P, int T,
                                                          int n, int K, float* __restrict__ dl) {
-    const int t = blockIdx.x * 256 + threadIdx.x;
+    // one wave per token: lane u adds the partial sums u, u + 64, ... of each
+    // slot's row, then a butterfly (a fixed order) completes them
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     float dg[kMaxTopK], gs[kMaxTopK];
     float S = 0.0f;
@@ -577,17 +581,24 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(const int32_t* __restri
         gs[s] = 0.0f;
         if (s < K) {
             const int p = row_of[t * K + s];
+            float v = 0.0f;
             if (p >= 0)
-                for (int u = 0; u < nut; ++u) dg[s] += dgp[static_cast<int64_t>(u) * P + p];
+                for (int u = lane; u < nut; u += 64) v += dgp[static_cast<int64_t>(u) * P + p];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            dg[s] = v;
             gs[s] = gate[t * K + s];
             S = fmaf(gs[s], dg[s], S);
         }
     }
     float* row = dl + static_cast<int64_t>(t) * n;
-    for (int e = 0; e < n; ++e) row[e] = 0.0f;
+    if (lane < n) {
+        float v = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
-        if (s < K) row[idx[t * K + s]] = gs[s] * (dg[s] - S);
+        for (int s = 0; s < kMaxTopK; ++s)
+            if (s < K && idx[t * K + s] == lane) v = gs[s] * (dg[s] - S);
+        row[lane] = v;
+    }
 }
 
 // dx[t] = sum_s (dxp + dxp_hi)[row_of[t, s]] (slot order) + sum_s dl[t, e_s] W_g[:, e_s], one
@@ -677,38 +688,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 constexpr int kDwgTokens = 64;  // tokens per partial sum of dW_g
 
 // part[chunk][k][e] = sum over the chunk's tokens of x[t][k] dl[t][e]
-__global__ __launch_bounds__(256) void bwd_dwg_partial_kernel(const bf16_t* __restrict__ x,
-                                                              const float* __restrict__ dl, int T, int d, int n,
-                                                              float* __restrict__ part) {
+// One wave per (512 columns of x, kDwgTokens tokens): lane l sums columns
+// 8l .. 8l + 7 of its block (one 16-byte load of x per token) against the
+// chunk's dl rows, in token order.
+__global__ __launch_bounds__(64) void bwd_dwg_partial_kernel(const bf16_t* __restrict__ x,
+                                                             const float* __restrict__ dl, int T, int d, int n,
+                                                             float* __restrict__ part) {
     __shared__ float s_dl[kDwgTokens * kMaxExperts];
-    const int k = blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x;
+    const int k0 = blockIdx.x * 512 + 8 * lane;
     const int t0 = blockIdx.y * kDwgTokens;
     const int nt = min(kDwgTokens, T - t0);
-    for (int i = threadIdx.x; i < nt * n; i += 256) s_dl[i] = dl[static_cast<int64_t>(t0) * n + i];
+    for (int i = lane; i < nt * n; i += 64) s_dl[i] = dl[static_cast<int64_t>(t0) * n + i];
     __syncthreads();
-    if (k >= d) return;
-    float acc[kMaxExperts];
+    float acc[8][kMaxExperts];
 #pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) acc[e] = 0.0f;
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e) acc[j][e] = 0.0f;
     for (int i = 0; i < nt; ++i) {
-        const float xv = bf16_to_f32(x[static_cast<int64_t>(t0 + i) * d + k]);
+        float xv[8];
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t0 + i) * d + k0), xv);
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e) {
+            if (e < n) {
+                const float w = s_dl[i * n + e];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j][e] = fmaf(xv[j], w, acc[j][e]);
+            }
+        }
+    }
+    float* out = part + (static_cast<int64_t>(blockIdx.y) * d + k0) * n;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int e = 0; e < kMaxExperts; ++e)
-            if (e < n) acc[e] = fmaf(xv, s_dl[i * n + e], acc[e]);
-    }
-    float* out = part + (static_cast<int64_t>(blockIdx.y) * d + k) * n;
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e)
-        if (e < n) out[e] = acc[e];
+            if (e < n) out[j * n + e] = acc[j][e];
 }
 
+// dW_g = the chunk partials summed in chunk order; four outputs per thread.
 __global__ __launch_bounds__(256) void bwd_dwg_reduce_kernel(const float* __restrict__ part, int chunks, int dn,
                                                              float* __restrict__ dwg) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
     if (i >= dn) return;
-    float s = 0.0f;
-    for (int c = 0; c < chunks; ++c) s += part[static_cast<int64_t>(c) * dn + i];
-    dwg[i] = s;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int c = 0; c < chunks; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(part + static_cast<int64_t>(c) * dn + i);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    *reinterpret_cast<float4*>(dwg + i) = s;
 }
 
 __global__ __launch_bounds__(256) void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -846,7 +875,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
         return err;
 
     // router gradient, dx, dW_g
-    bwd_router_kernel<<<(T + 255) / 256, 256, 0, st>>>(w.idx, w.gate, w.row_of, w.dgp, F / kTU, P, T, n, K, w.dl);
+    bwd_router_kernel<<<(T + 3) / 4, 256, 0, st>>>(w.idx, w.gate, w.row_of, w.dgp, F / kTU, P, T, n, K, w.dl);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     {
         const float* hi = w.dxp + static_cast<int64_t>(P) * d;
@@ -860,9 +889,9 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int chunks = (T + kDwgTokens - 1) / kDwgTokens;
-    bwd_dwg_partial_kernel<<<dim3((d + 255) / 256, chunks), 256, 0, st>>>(xb, w.dl, T, d, n, w.dwg_part);
+    bwd_dwg_partial_kernel<<<dim3(d / 512, chunks), 64, 0, st>>>(xb, w.dl, T, d, n, w.dwg_part);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    bwd_dwg_reduce_kernel<<<(d * n + 255) / 256, 256, 0, st>>>(w.dwg_part, chunks, d * n, dwg);
+    bwd_dwg_reduce_kernel<<<(d * n / 4 + 255) / 256, 256, 0, st>>>(w.dwg_part, chunks, d * n, dwg);
     return hipGetLastError();
 }
 
