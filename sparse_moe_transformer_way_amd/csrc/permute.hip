@@ -21,7 +21,12 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
 // NE expert slots; experts 0..n-1 are real, any other index is ignored.
-template <int NE>
+// A thread's assignments (at most HELD = 8, or at most 32 with HELD = 0) are
+// loaded once, all at the same time, and kept in registers for the scatter;
+// with HELD = 0 and more than 32 per thread they are read as they are counted
+// and read again for the scatter.  (A compile-time 16 or 32 held ran out of
+// the 128 registers a 1024-thread block allows and spilled.)
+template <int NE, int HELD>
 __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int TK, int n,
                                                            int tile_m, int P_max,
                                                            int32_t* __restrict__ counts,
@@ -39,13 +44,27 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     const int a0 = min(TK, tid * per);
     const int a1 = min(TK, a0 + per);
 
+    constexpr int kHeld = HELD > 0 ? HELD : 32;
+    const bool held = HELD > 0 || per <= kHeld;
+    int ev[kHeld];
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i) ev[i] = a0 + i < a1 ? idx[a0 + i] : -1;
+    }
     int c[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) c[e] = 0;
-    for (int a = a0; a < a1; ++a) {
-        const int e = idx[a];
+    if (held) {
 #pragma unroll
-        for (int j = 0; j < NE; ++j) c[j] += (e == j && j < n) ? 1 : 0;
+        for (int i = 0; i < kHeld; ++i)
+#pragma unroll
+            for (int j = 0; j < NE; ++j) c[j] += (ev[i] == j && j < n) ? 1 : 0;
+    } else {
+        for (int a = a0; a < a1; ++a) {
+            const int e = idx[a];
+#pragma unroll
+            for (int j = 0; j < NE; ++j) c[j] += (e == j && j < n) ? 1 : 0;
+        }
     }
 
     // Inclusive scan of each expert's count across the wave.
@@ -93,8 +112,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     int pos[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) pos[e] = s_off[e] + s_wave[wave][e] + incl[e] - c[e];
-    for (int a = a0; a < a1; ++a) {
-        const int e = idx[a];
+    auto place = [&](int a, int e) {
         int p = -1;
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
@@ -105,6 +123,13 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
         }
         if (p >= 0) row_src[p] = a;
         row_of[a] = p;
+    };
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i)
+            if (a0 + i < a1) place(a0 + i, ev[i]);
+    } else {
+        for (int a = a0; a < a1; ++a) place(a, idx[a]);
     }
 
     // Padding rows of every segment, then everything past the last segment.
@@ -170,10 +195,18 @@ hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_
         permute_wave_kernel<<<1, 64, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
         return hipGetLastError();
     }
-    if (s.n <= 8)
-        permute_kernel<8><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
-    else
-        permute_kernel<16><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of);
+    // assignments per thread: up to 8 take the kernel that holds exactly 8
+    const int per = (TK + kThreads - 1) / kThreads;
+    const int held = per <= 8 ? 8 : 0;
+#define MOE_PERMUTE(NE, H) \
+    permute_kernel<NE, H><<<1, kThreads, 0, st>>>(idx, TK, s.n, tile_m, P_max, counts, offsets, row_src, row_of)
+    if (s.n <= 8) {
+        if (held == 8) MOE_PERMUTE(8, 8);
+        else MOE_PERMUTE(8, 0);
+    } else {
+        MOE_PERMUTE(16, 0);  // held 8 with 16 expert slots spills
+    }
+#undef MOE_PERMUTE
     return hipGetLastError();
 }
 

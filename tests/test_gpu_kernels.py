@@ -96,7 +96,10 @@ def _random_idx(T, seed, skew=False):
     return np.stack([rng.permutation(8)[:2] for _ in range(T)]).astype(np.int32).reshape(T, 2)
 
 
+# 2000, 6000, 16000 and 17000 tokens: each thread of the one-block kernel holds
+# up to 8 or up to 32 assignments in registers, or (above 32768) reads them twice.
 @pytest.mark.parametrize("T,tile_m,skew", [(0, 16, False), (1, 16, False), (31, 16, False),
+                                           (6000, 256, False), (16000, 256, True), (17000, 256, False),
                                            (32, 16, False), (32, 256, False), (32, 16, True),
                                            (33, 16, False), (37, 16, False),
                                            (300, 256, False), (2000, 256, False),
