@@ -205,3 +205,14 @@ def test_backward_descriptor_rules():
     assert lib.moe_layer_backward(pb, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4096, FAKE, FAKE, FAKE,
                                   FAKE, FAKE, 10, None) == 3         # workspace too small
     assert lib.moe_layer_backward(pb, -1, *args, FAKE, 1 << 30, None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU: --gpus above 1 exits with a message and a
+    non-zero status before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "no multi-GPU path" in r.stderr
