@@ -380,6 +380,55 @@ def test_moe_block_residual():
     np.testing.assert_allclose(h_next - x, ref, rtol=1e-4, atol=1e-5)
 
 
+def _bf16(v):
+    """Round float64 values to bf16 with torch's cast (an implementation
+    independent of the oracle's), returned as float64."""
+    return torch.tensor(np.asarray(v, np.float64), dtype=torch.float64).to(torch.float32) \
+        .to(torch.bfloat16).double().numpy()
+
+
+def test_moe_block_bf16_storage_hand_placed():
+    """Where the stack's bf16 storage rounds: the normalised x is rounded to bf16
+    after the norm (it is the stored input of the layer), and the block output
+    h + y is rounded once after the residual add.  Identical identity experts
+    and an all-zero router (gates exactly 1/2, 1/2) make y = SiLU(x) * x, which
+    is written out here in float64 from the closed form sigma(z) = 1/(1+e^-z)."""
+    d = n = 4
+    eye = np.eye(d, dtype=np.float32)
+    w = np.stack([eye] * n)
+    wg = np.zeros((d, n), np.float32)
+    h = np.array([[3.0, 4.0, 0.5, -1.25], [-2.0, 0.375, 1.5, 2.75], [0.125, -7.0, 6.5, 1.0]], np.float32)
+    assert (_bf16(h) == h).all()
+    h64 = h.astype(np.float64)
+    x_exact = h64 / np.sqrt((h64 ** 2).mean(axis=1, keepdims=True) + 1e-5)
+    x_hand = _bf16(x_exact)
+
+    def e(x):
+        return x * x / (1.0 + np.exp(-x))
+
+    want = _bf16(h64 + e(x_hand))
+    # the case tells the placements apart: no rounding of x, no rounding of the
+    # output, and rounding y before the residual add all give other values
+    assert (x_hand != x_exact).any()
+    assert (_bf16(h64 + e(x_exact)) != want).any()
+    assert (h64 + e(x_hand) != want).any()
+    assert (h64 + _bf16(e(x_hand)) != want).any() or (_bf16(h64 + _bf16(e(x_hand))) != want).any()
+    # no value sits near a bf16 rounding boundary, so fp32 evaluation order cannot flip it
+    v = h64 + e(x_hand)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(v))) - 7)
+    frac = np.abs(v / ulp - np.round(v / ulp))
+    assert (np.abs(frac - 0.5) > 1e-3).all()
+
+    h_next, out = oracle.moe_block(h, wg, w, w, w, K=2, bf16_storage=True)
+    np.testing.assert_array_equal(out["x"], x_hand)
+    np.testing.assert_array_equal(out["gates"], 0.5)
+    np.testing.assert_array_equal(h_next, want)
+    # without bf16 storage the same block keeps fp32 values
+    h32, out32 = oracle.moe_block(h, wg, w, w, w, K=2, bf16_storage=False)
+    np.testing.assert_allclose(out32["x"], x_exact, rtol=1e-6)
+    np.testing.assert_allclose(h32, h64 + e(x_exact), rtol=1e-6)
+
+
 # ---------------------------------------------------------------------------
 # The pages' printed parameter counts
 # ---------------------------------------------------------------------------
