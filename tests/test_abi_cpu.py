@@ -136,9 +136,97 @@ def test_layer_forward_workspace_checks():
 def test_binding_requires_device_tensors():
     import torch
     d = moe.make_desc(4096, 14336)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="device tensor"):
         moe.moe_router_topk(d, torch.zeros(2, 4096, dtype=torch.bfloat16),
                             torch.zeros(4096, 8))
+
+
+def _binding_calls(bad):
+    """Each binding called with CPU tensors of the right shapes, except for the
+    one argument named ``bad``, which gets one row too few (or the wrong dtype
+    when bad ends in ':dtype').  d = 512, F = 1024, n = 8, K = 2, T = 40."""
+    import torch
+    bf, f32, i32, u8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+    d, F, n, K, T = 512, 1024, 8, 2, 40
+    desc = moe.make_desc(d, F)
+    P16 = moe.moe_max_permuted_rows(desc, T, 16)
+
+    def t(name, shape, dt):
+        if bad == name:
+            shape = (shape[0] - 1,) + tuple(shape[1:]) if shape and shape[0] > 0 else (1,)
+        if bad == name + ":dtype":
+            dt = f32 if dt != f32 else bf
+        return torch.zeros(shape, dtype=dt)
+
+    return {
+        "moe_router_topk": lambda: moe.moe_router_topk(
+            desc, torch.zeros(T, d, dtype=bf), t("w_gate", (d, n), f32), t("topk_idx", (T, K), i32),
+            t("topk_gate", (T, K), f32), t("logits_out", (T, n), f32)),
+        "moe_permute": lambda: moe.moe_permute(
+            desc, torch.zeros(T, K, dtype=i32), 16, t("counts", (n,), i32), t("offsets", (n + 1,), i32),
+            t("row_src", (P16,), i32), t("row_of", (T, K), i32)),
+        "moe_expert_gate_up": lambda: moe.moe_expert_gate_up(
+            desc, T, 16, t("x", (T, d), bf), t("row_src", (P16,), i32), t("counts", (n,), i32),
+            t("offsets", (n + 1,), i32), t("w1", (n, F, d), bf), t("w3", (n, F, d), bf), t("h", (P16, F), bf)),
+        "moe_expert_down": lambda: moe.moe_expert_down(
+            desc, T, 16, t("h", (P16, F), bf), t("counts", (n,), i32), t("offsets", (n + 1,), i32),
+            t("w2", (n, d, F), bf), t("y_perm", (P16, d), f32)),
+        "moe_grouped_swiglu": lambda: moe.moe_grouped_swiglu(
+            desc, T, 16, t("x", (T, d), bf), t("row_src", (P16,), i32), t("counts", (n,), i32),
+            t("offsets", (n + 1,), i32), t("w1", (n, F, d), bf), t("w3", (n, F, d), bf), t("w2", (n, d, F), bf),
+            t("h", (P16, F), bf), t("y_perm", (P16, d), f32)),
+        "moe_combine": lambda: moe.moe_combine(
+            desc, t("y_perm", (P16, d), f32), torch.zeros(T, K, dtype=i32), t("topk_gate", (T, K), f32),
+            t("residual", (T, d), bf), t("y", (T, d), bf)),
+        "moe_layer_forward": lambda: moe.moe_layer_forward(
+            desc, torch.zeros(T, d, dtype=bf), t("w_gate", (d, n), f32), t("w1", (n, F, d), bf),
+            t("w3", (n, F, d), bf), t("w2", (n, d, F), bf), t("residual", (T, d), bf), t("y", (T, d), bf),
+            t("topk_idx_out", (T, K), i32), t("topk_gate_out", (T, K), f32), t("counts_out", (n,), i32),
+            workspace=torch.zeros(moe.moe_workspace_size(desc, T, 0), dtype=u8)),
+        "moe_block_forward": lambda: moe.moe_block_forward(
+            desc, torch.zeros(T, d, dtype=bf), t("w_gate", (d, n), f32), t("w1", (n, F, d), bf),
+            t("w3", (n, F, d), bf), t("w2", (n, d, F), bf), h_out=t("h_out", (T, d), bf),
+            topk_idx_out=t("topk_idx_out", (T, K), i32), counts_out=t("counts_out", (n,), i32),
+            workspace=torch.zeros(16, dtype=u8)),
+        "moe_layer_backward": lambda: moe.moe_layer_backward(
+            desc, torch.zeros(T, d, dtype=bf), t("w_gate", (d, n), f32), t("w1", (n, F, d), bf),
+            t("w3", (n, F, d), bf), t("w2", (n, d, F), bf), t("dy", (T, d), bf), t("dx", (T, d), bf),
+            t("dw_gate", (d, n), f32), t("dw1", (n, F, d), f32), t("dw3", (n, F, d), f32),
+            t("dw2", (n, d, F), f32), workspace=torch.zeros(16, dtype=u8)),
+    }
+
+
+BAD_ARGS = [("moe_router_topk", "w_gate"), ("moe_router_topk", "topk_gate"), ("moe_router_topk", "logits_out"),
+            ("moe_permute", "row_src"), ("moe_permute", "offsets"), ("moe_permute", "row_of"),
+            ("moe_expert_gate_up", "x"), ("moe_expert_gate_up", "h"), ("moe_expert_gate_up", "w3"),
+            ("moe_expert_gate_up", "row_src"), ("moe_expert_down", "y_perm"), ("moe_expert_down", "w2"),
+            ("moe_grouped_swiglu", "w1"), ("moe_grouped_swiglu", "y_perm"), ("moe_combine", "y"),
+            ("moe_combine", "residual"), ("moe_combine", "topk_gate"), ("moe_layer_forward", "w2"),
+            ("moe_layer_forward", "y"), ("moe_layer_forward", "counts_out"), ("moe_block_forward", "h_out"),
+            ("moe_block_forward", "w1"), ("moe_layer_backward", "dw2"), ("moe_layer_backward", "dy")]
+
+
+@pytest.mark.parametrize("fn,bad", BAD_ARGS)
+def test_binding_checks_shapes_before_any_call(fn, bad):
+    """A tensor smaller than the call would touch is refused by the binding
+    (the C ABI sees raw pointers only), before any device check."""
+    with pytest.raises(ValueError, match=f"{bad} has shape"):
+        _binding_calls(bad)[fn]()
+
+
+@pytest.mark.parametrize("fn,bad", [("moe_router_topk", "w_gate:dtype"), ("moe_expert_gate_up", "w1:dtype"),
+                                    ("moe_layer_forward", "topk_idx_out:dtype")])
+def test_binding_checks_dtypes(fn, bad):
+    with pytest.raises(TypeError):
+        _binding_calls(bad)[fn]()
+
+
+@pytest.mark.parametrize("fn", ["moe_router_topk", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
+                                "moe_grouped_swiglu", "moe_combine", "moe_layer_forward", "moe_block_forward",
+                                "moe_layer_backward"])
+def test_binding_well_shaped_host_tensors_still_refused(fn):
+    with pytest.raises(ValueError, match="device tensor"):
+        _binding_calls(None)[fn]()
 
 
 def test_fp8_descriptor_rules():
