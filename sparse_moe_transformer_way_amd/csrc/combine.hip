@@ -18,7 +18,7 @@ namespace {
 // One 4-column group c of token t's output from its loaded slot values a[s]
 // (the two K-parts already added; dropped slots are zero) and the residual.
 template <bool BF16, int K, bool RES>
-__device__ __forceinline__ void combine_store(const float4 (&a)[K], const float (&g)[K], const void* __restrict__ residual,
+__device__ __forceinline__ void combine_store(const float4 (&a)[K], const float (&g)[K], const void* residual,
                                               void* y, size_t o) {
     float v[4] = {g[0] * a[0].x, g[0] * a[0].y, g[0] * a[0].z, g[0] * a[0].w};
 #pragma unroll
@@ -66,12 +66,15 @@ __device__ __forceinline__ void combine_load(const float4* const (&p)[K], const 
 // One block of 256 threads per token.  Full passes take U groups per thread
 // with every load issued before the first store (a decode row, d = 4096, is
 // one pass), then a plain loop takes what is left.  HI: y_perm has a second
-// K-part to add; RES: a residual is added.
+// K-part to add; RES: a residual is added.  residual may be y itself (the
+// in-place update of a residual stream): neither is marked __restrict__, and
+// each element of the residual is read by the thread that writes it, before
+// that write.
 template <bool BF16, int K, bool HI, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
-                                                      const void* __restrict__ residual, void* y,
+                                                      const void* residual, void* y,
                                                       int d, const float* __restrict__ y_perm_hi) {
     constexpr int U = 4;
     const int t = blockIdx.x;
