@@ -53,13 +53,43 @@ def check_full(inp, tol):
     ("bf16", 65, 512, 1024),    # first T on the tiled kernels, few rows per expert
     ("bf16", 1000, 512, 1024),  # tiled kernels, ~250 rows per expert
     ("bf16", 2500, 1024, 512),
-    ("bf16", 1150, 512, 1024),  # short expert tails past full 256-row tiles
+    ("bf16", 1150, 512, 1024),  # short expert tails (the tiled kernel keeps them at d = 512)
     ("bf16", 2100, 1024, 512),
 ])
 def test_layer_small(dtype, T, d, F):
     init = "fanin" if dtype == "f32" else "mixtral"
     inp = margin_filtered(mi.make_layer(T, d, F, dtype=dtype, init=init, seed=T + d, workload=300))
     check_full(inp, TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def down_tail_split_pays(counts, d, F, T, K=2, n=8):
+    """Whether moe_layer_forward's tiled down projection hands the experts'
+    short tails (at most 64 rows past their full 256-row tiles) to the
+    streaming pass: it does when that lowers the number of rounds of 256
+    workgroups, with K cut in two when the tiles fill fewer than four rounds.
+    Returns (K parts, pays)."""
+    P = T * K + n * 255
+    n_tt, n_wt = -(-P // 256), d // 256
+    ks = 2 if (n_tt * n_wt < 4 * 256 and (F // 2) % 256 == 0) else 1
+    per_tile_row = n_wt * ks
+    without = sum(-(-c // 256) for c in counts)
+    with_tail = sum(c // 256 if 0 < c % 256 <= 64 else -(-c // 256) for c in counts)
+    return ks, -(-with_tail * per_tile_row // 256) < -(-without * per_tile_row // 256)
+
+
+# d = 4096 with a small F at T = 1150: every expert gets 255-316 rows, so
+# dropping the tail tiles halves the down projection's rounds.  With F = 1536
+# the tail pass runs in one K part and clears its rows of the second partial;
+# with F = 2048 it cuts K in two like the tiled kernel.
+@pytest.mark.parametrize("F,seed", [(1536, 1), (2048, 0)])
+def test_layer_down_tail_pass(F, seed):
+    T, d = 1150, 4096
+    inp = margin_filtered(mi.make_layer(T, d, F, seed=seed, workload=305))
+    counts = np.bincount(oracle.gating(inp.x.float().numpy(), inp.wg.numpy())[1].ravel(), minlength=8)
+    ks, pays = down_tail_split_pays(counts.tolist(), d, F, T)
+    assert ks == 2 and pays, (counts, ks, pays)
+    err = check_full(inp, TOL_BF16)
+    print(f"down tail pass, F={F}: counts {counts.tolist()}, max per-token rel err {err:.3e}")
 
 
 def test_tiny_workload():
