@@ -197,6 +197,31 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing: its
+ * intermediates live in a scratch array of MOE_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds in each GPU's memory until the process ends (one
+ * copy per device, taken on the device current at the call, which must be
+ * the device of the buffers and the stream).  The caller still passes inputs
+ * and outputs, exactly as for moe_layer_forward.
+ *   - T with moe_workspace_size(desc, T, 0) > MOE_NOALLOC_SCRATCH_BYTES returns
+ *     MOE_ERR_WORKSPACE_TOO_SMALL (at d = 4096, F = 14336, n = 8, K = 2 that
+ *     is every T above 64; decode batches up to 64 tokens fit).
+ *   - Every call on a GPU shares that GPU's scratch: calls that overlap on one
+ *     GPU (other streams, other host threads) race and must be serialised by
+ *     the caller.  Nothing needs clearing between calls: every scratch byte a
+ *     call reads is written earlier in the same call.
+ *   - FP8 descriptors return MOE_ERR_INVALID_ARGUMENT.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                       const float* w_gate, const void* w1, const void* w3,
+                                       const void* w2, const void* residual, void* y,
+                                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                                       void* stream);
+
+/*
  * One decoder MoE block with attention omitted:
  *     h_out = h + moe_layer(RMSNorm(h))
  * (paper-graph-ui page, section 3.2: the MoE output is added to the residual

@@ -16,14 +16,14 @@ from typing import Optional
 import torch
 
 from ._lib import (  # noqa: F401
-    LIB_PATH, MOE_BF16, MOE_FP8_E4M3, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
+    LIB_PATH, MOE_BF16, MOE_FP8_E4M3, MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE_TOO_SMALL, MOE_F32, MOE_OK, LayerDesc, MoeError, SIGNATURES, lib,
 )
 
 __all__ = [
     "make_desc", "moe_version", "moe_default_tile_m", "moe_max_permuted_rows", "moe_workspace_size",
     "moe_router_topk", "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_swiglu",
-    "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_block_workspace_size",
+    "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_block_workspace_size",
     "moe_block_forward", "moe_quantize_fp8", "moe_expert_gate_up_fp8", "moe_expert_down_fp8",
     "moe_layer_forward_fp8", "moe_backward_workspace_size", "moe_layer_backward", "LayerDesc", "MoeError",
 ]
@@ -319,6 +319,31 @@ def moe_layer_forward(desc, x, w_gate, w1, w3, w2, residual=None, y=None, topk_i
                                     topk_gate_out, counts_out),
                   ("workspace", workspace, (workspace.numel(),), torch.uint8, False))
     _check(fn, lib.moe_layer_forward(desc, T, *p, workspace.numel(), _stream(stream)))
+    return y, topk_idx_out, topk_gate_out, counts_out
+
+
+def moe_layer_forward_noalloc(desc, x, w_gate, w1, w3, w2, residual=None, y=None, topk_idx_out=None,
+                              topk_gate_out=None, counts_out=None, stream=None):
+    """The whole layer with the library's per-GPU scratch instead of a workspace
+    (the C call allocates nothing; outputs not passed in are allocated here).
+    Calls that overlap on one GPU race on that scratch.  Returns
+    (y, topk_idx, topk_gate, counts)."""
+    fn = "moe_layer_forward_noalloc"
+    T = x.shape[0]
+    dt = _act_dtype(desc)
+    dev = x.device
+    n, K = desc.n_experts, desc.top_k
+    if y is None:
+        y = torch.empty((T, desc.d_model), dtype=dt, device=dev)
+    if topk_idx_out is None:
+        topk_idx_out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_gate_out is None:
+        topk_gate_out = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if counts_out is None:
+        counts_out = torch.empty(n, dtype=torch.int32, device=dev)
+    p = _validate(fn, *_layer_specs(desc, T, x, w_gate, w1, w3, w2, residual, y, topk_idx_out,
+                                    topk_gate_out, counts_out))
+    _check(fn, lib.moe_layer_forward_noalloc(desc, T, *p, _stream(stream)))
     return y, topk_idx_out, topk_gate_out, counts_out
 
 

@@ -21,6 +21,8 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FP8_E4M3 = 2
 
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20  # scratch of moe_layer_forward_noalloc per GPU
+
 
 class LayerDesc(ctypes.Structure):
     """moe_layer_desc_t."""
@@ -54,6 +56,7 @@ SIGNATURES = {
     "moe_rmsnorm": (_i32, [_i32, _i32, _i32, _p, ctypes.c_float, _p, _p]),
     "moe_layer_forward": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                  ctypes.c_size_t, _p]),
+    "moe_layer_forward_noalloc": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_block_workspace_size": (ctypes.c_size_t, [_desc, _i32]),
     "moe_block_forward": (_i32, [_desc, _i32, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p,
                                  ctypes.c_size_t, _p]),

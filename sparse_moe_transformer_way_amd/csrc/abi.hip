@@ -1,6 +1,8 @@
 // C ABI of the MoE layer library: argument validation, workspace carving and
 // launch sequencing.  Every entry point validates synchronously, enqueues its
 // kernels on the caller's stream and returns without synchronising.
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -124,28 +126,28 @@ struct ExpertWeights {
     const float* s2;
 };
 
-moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
-                           const ExpertWeights& ew, const void* residual, void* y, int32_t* topk_idx_out,
-                           float* topk_gate_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-    moe_status_t s;
-    if ((s = check_T(T, desc)) != MOE_OK) return s;
-    if (T == 0) return MOE_OK;
+// Argument checks of the layer (everything but the workspace), before any launch.
+moe_status_t check_layer_args(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                              const ExpertWeights& ew, const void* residual, const void* y) {
     const bool fp8 = is_fp8(desc);
     if (x == nullptr || w_gate == nullptr || ew.w1 == nullptr || ew.w3 == nullptr || ew.w2 == nullptr ||
-        y == nullptr || workspace == nullptr)
+        y == nullptr)
         return MOE_ERR_INVALID_ARGUMENT;
     if (fp8 && (ew.s1 == nullptr || ew.s3 == nullptr || ew.s2 == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
     if (x == y) return MOE_ERR_INVALID_ARGUMENT;
-    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(ew.w1) || !aligned16(ew.w3) || !aligned16(ew.w2) ||
         !aligned16(y) || (residual != nullptr && !aligned16(residual)))
         return MOE_ERR_INVALID_ARGUMENT;
     if (fp8 && (!aligned16(ew.s1) || !aligned16(ew.s3) || !aligned16(ew.s2))) return MOE_ERR_INVALID_ARGUMENT;
-    const int tile_m = default_tile(desc, T);
-    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
-    if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    (void)T;
+    return MOE_OK;
+}
 
+// The layer's launches on a checked workspace of w.bytes bytes.
+moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, const LayerWs& w, const void* x,
+                       const float* w_gate, const ExpertWeights& ew, const void* residual, void* y,
+                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* stream) {
+    const bool fp8 = is_fp8(desc);
     const moe::Shape sh = shape_of(desc, T);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
@@ -174,6 +176,52 @@ moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* 
     if (moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st, parts == 2 ? w.y_perm_hi : nullptr) !=
         hipSuccess)
         return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
+                           const ExpertWeights& ew, const void* residual, void* y, int32_t* topk_idx_out,
+                           float* topk_gate_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    moe_status_t s;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if ((s = check_layer_args(desc, T, x, w_gate, ew, residual, y)) != MOE_OK) return s;
+    if (workspace == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    const int tile_m = default_tile(desc, T);
+    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
+    if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return run_layer(desc, T, tile_m, w, x, w_gate, ew, residual, y, topk_idx_out, topk_gate_out, counts_out,
+                     stream);
+}
+
+// ---- Scratch of moe_layer_forward_noalloc: one array per GPU in the code
+// object's device memory, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it names a stand-in, not
+// device memory): each device's address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+constexpr size_t kNoAllocBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status_t device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return MOE_OK;
 }
 
@@ -330,6 +378,26 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
     if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
     return layer_forward(desc, T, x, w_gate, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr}, residual, y,
                          topk_idx_out, topk_gate_out, counts_out, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                       const float* w_gate, const void* w1, const void* w3, const void* w2,
+                                       const void* residual, void* y, int32_t* topk_idx_out,
+                                       float* topk_gate_out, int32_t* counts_out, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((s = check_T(T, desc)) != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    const ExpertWeights ew{w1, w3, w2, nullptr, nullptr, nullptr};
+    if ((s = check_layer_args(desc, T, x, w_gate, ew, residual, y)) != MOE_OK) return s;
+    const int tile_m = default_tile(desc, T);
+    if (carve_layer(desc, T, tile_m, nullptr).bytes > kNoAllocBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if ((s = device_scratch(&ws)) != MOE_OK) return s;
+    const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(ws));
+    return run_layer(desc, T, tile_m, w, x, w_gate, ew, residual, y, topk_idx_out, topk_gate_out, counts_out,
+                     stream);
 }
 
 size_t moe_block_workspace_size(const moe_layer_desc_t* desc, int32_t T) {
