@@ -197,6 +197,24 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_layer_forward with a HIP event recorded on `stream` before the router and
+ * after each of the layer's five stages, so that each stage's duration inside
+ * the layer's own launch sequence can be measured (events[i+1] - events[i]:
+ * router + top-k, grouping, gate/up + SwiGLU, down projection with its K split
+ * and tail pass when the layer takes them, combine).
+ *   events  6 hipEvent_t handles, created by the caller (timing enabled);
+ *           none may be NULL.  Everything else is as for moe_layer_forward
+ *           (bf16 and fp32 descriptors; FP8 returns MOE_ERR_INVALID_ARGUMENT).
+ * T == 0 records nothing.
+ */
+moe_status_t moe_layer_forward_timed(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                     const float* w_gate, const void* w1, const void* w3,
+                                     const void* w2, const void* residual, void* y,
+                                     int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                                     void* workspace, size_t workspace_bytes, void* const* events,
+                                     void* stream);
+
+/*
  * moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The call itself allocates nothing: its

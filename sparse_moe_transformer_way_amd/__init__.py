@@ -11,6 +11,7 @@ are not passed in are allocated with torch.empty on the inputs' device.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -23,7 +24,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "make_desc", "moe_version", "moe_default_tile_m", "moe_max_permuted_rows", "moe_workspace_size",
     "moe_router_topk", "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_swiglu",
-    "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_block_workspace_size",
+    "moe_combine", "moe_rmsnorm", "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_noalloc", "moe_block_workspace_size",
     "moe_block_forward", "moe_quantize_fp8", "moe_expert_gate_up_fp8", "moe_expert_down_fp8",
     "moe_layer_forward_fp8", "moe_backward_workspace_size", "moe_layer_backward", "LayerDesc", "MoeError",
 ]
@@ -319,6 +320,38 @@ def moe_layer_forward(desc, x, w_gate, w1, w3, w2, residual=None, y=None, topk_i
                                     topk_gate_out, counts_out),
                   ("workspace", workspace, (workspace.numel(),), torch.uint8, False))
     _check(fn, lib.moe_layer_forward(desc, T, *p, workspace.numel(), _stream(stream)))
+    return y, topk_idx_out, topk_gate_out, counts_out
+
+
+def moe_layer_forward_timed(desc, x, w_gate, w1, w3, w2, events, residual=None, y=None, topk_idx_out=None,
+                            topk_gate_out=None, counts_out=None, workspace=None, stream=None):
+    """moe_layer_forward with six torch.cuda.Event objects (timing enabled, each
+    recorded at least once so that it exists) recorded on the stream before the
+    router and after each of the five stages.  Returns (y, topk_idx, topk_gate, counts)."""
+    fn = "moe_layer_forward_timed"
+    if len(events) != 6:
+        raise ValueError(f"{fn}: expected 6 events, got {len(events)}")
+    handles = [e.cuda_event for e in events]
+    if not all(handles):
+        raise ValueError(f"{fn}: every event must have been recorded once (created) before the call")
+    T = x.shape[0]
+    dt = _act_dtype(desc)
+    dev = x.device
+    n, K = desc.n_experts, desc.top_k
+    if y is None:
+        y = torch.empty((T, desc.d_model), dtype=dt, device=dev)
+    if topk_idx_out is None:
+        topk_idx_out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_gate_out is None:
+        topk_gate_out = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if counts_out is None:
+        counts_out = torch.empty(n, dtype=torch.int32, device=dev)
+    workspace = _workspace(fn, workspace, lib.moe_workspace_size(desc, T, 0), dev)
+    p = _validate(fn, *_layer_specs(desc, T, x, w_gate, w1, w3, w2, residual, y, topk_idx_out,
+                                    topk_gate_out, counts_out),
+                  ("workspace", workspace, (workspace.numel(),), torch.uint8, False))
+    arr = (ctypes.c_void_p * 6)(*handles)
+    _check(fn, lib.moe_layer_forward_timed(desc, T, *p, workspace.numel(), arr, _stream(stream)))
     return y, topk_idx_out, topk_gate_out, counts_out
 
 

@@ -56,6 +56,8 @@ SIGNATURES = {
     "moe_rmsnorm": (_i32, [_i32, _i32, _i32, _p, ctypes.c_float, _p, _p]),
     "moe_layer_forward": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                  ctypes.c_size_t, _p]),
+    "moe_layer_forward_timed": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                       ctypes.c_size_t, _p, _p]),
     "moe_layer_forward_noalloc": (_i32, [_desc, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_block_workspace_size": (ctypes.c_size_t, [_desc, _i32]),
     "moe_block_forward": (_i32, [_desc, _i32, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p,

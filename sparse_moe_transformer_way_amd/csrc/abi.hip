@@ -144,17 +144,29 @@ moe_status_t check_layer_args(const moe_layer_desc_t* desc, int32_t T, const voi
 }
 
 // The layer's launches on a checked workspace of w.bytes bytes.
+// With `marks` (kLayerMarks events, or nullptr) an event is recorded on the
+// stream before the router and after each stage.
+constexpr int kLayerMarks = 6;
+
 moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, const LayerWs& w, const void* x,
                        const float* w_gate, const ExpertWeights& ew, const void* residual, void* y,
-                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* stream) {
+                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out, void* stream,
+                       void* const* marks = nullptr) {
     const bool fp8 = is_fp8(desc);
     const moe::Shape sh = shape_of(desc, T);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    int mark = 0;
+    auto record = [&]() {
+        return marks == nullptr || hipEventRecord(static_cast<hipEvent_t>(marks[mark++]), st) == hipSuccess;
+    };
     int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : w.idx;
     float* gate = topk_gate_out != nullptr ? topk_gate_out : w.gate;
     int32_t* counts = counts_out != nullptr ? counts_out : w.counts;
-    if (moe::launch_router_topk(sh, x, w_gate, idx, gate, nullptr, st) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st) != hipSuccess)
+    if (!record()) return MOE_ERR_HIP;
+    if (moe::launch_router_topk(sh, x, w_gate, idx, gate, nullptr, st) != hipSuccess || !record())
+        return MOE_ERR_HIP;
+    if (moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st) != hipSuccess ||
+        !record())
         return MOE_ERR_HIP;
     int parts = 1;
     if (fp8) {
@@ -162,19 +174,23 @@ moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, cons
         const auto* q3 = static_cast<const uint8_t*>(ew.w3);
         const auto* q2 = static_cast<const uint8_t*>(ew.w2);
         if (moe::launch_gate_up_fp8(sh, x, w.row_src, counts, w.offsets, q1, ew.s1, q3, ew.s3, w.h, st) !=
-            hipSuccess)
+                hipSuccess ||
+            !record())
             return MOE_ERR_HIP;
-        if (moe::launch_down_fp8(sh, w.h, counts, w.offsets, q2, ew.s2, w.y_perm, st) != hipSuccess)
+        if (moe::launch_down_fp8(sh, w.h, counts, w.offsets, q2, ew.s2, w.y_perm, st) != hipSuccess || !record())
             return MOE_ERR_HIP;
     } else {
-        if (moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, ew.w1, ew.w3, w.h, st) != hipSuccess)
+        if (moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, ew.w1, ew.w3, w.h, st) != hipSuccess ||
+            !record())
             return MOE_ERR_HIP;
         if (moe::launch_down(sh, tile_m, w.h, counts, w.offsets, ew.w2, w.y_perm, st, w.y_perm_hi, &parts) !=
-            hipSuccess)
+                hipSuccess ||
+            !record())
             return MOE_ERR_HIP;
     }
     if (moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st, parts == 2 ? w.y_perm_hi : nullptr) !=
-        hipSuccess)
+            hipSuccess ||
+        !record())
         return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -182,7 +198,7 @@ moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, cons
 moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* x, const float* w_gate,
                            const ExpertWeights& ew, const void* residual, void* y, int32_t* topk_idx_out,
                            float* topk_gate_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           void* stream, void* const* marks = nullptr) {
     moe_status_t s;
     if ((s = check_T(T, desc)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
@@ -193,7 +209,7 @@ moe_status_t layer_forward(const moe_layer_desc_t* desc, int32_t T, const void* 
     const LayerWs w = carve_layer(desc, T, tile_m, static_cast<char*>(workspace));
     if (workspace_bytes < w.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return run_layer(desc, T, tile_m, w, x, w_gate, ew, residual, y, topk_idx_out, topk_gate_out, counts_out,
-                     stream);
+                     stream, marks);
 }
 
 // ---- Scratch of moe_layer_forward_noalloc: one array per GPU in the code
@@ -378,6 +394,21 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, int32_t T, const vo
     if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;  // FP8 weights take the _fp8 entry points
     return layer_forward(desc, T, x, w_gate, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr}, residual, y,
                          topk_idx_out, topk_gate_out, counts_out, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_timed(const moe_layer_desc_t* desc, int32_t T, const void* x,
+                                     const float* w_gate, const void* w1, const void* w3, const void* w2,
+                                     const void* residual, void* y, int32_t* topk_idx_out, float* topk_gate_out,
+                                     int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                                     void* const* events, void* stream) {
+    moe_status_t s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (is_fp8(desc)) return MOE_ERR_INVALID_ARGUMENT;
+    if (events == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < kLayerMarks; ++i)
+        if (events[i] == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    return layer_forward(desc, T, x, w_gate, ExpertWeights{w1, w3, w2, nullptr, nullptr, nullptr}, residual, y,
+                         topk_idx_out, topk_gate_out, counts_out, workspace, workspace_bytes, stream, events);
 }
 
 moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, int32_t T, const void* x,

@@ -133,6 +133,28 @@ def test_layer_forward_workspace_checks():
                                  None, None, FAKE, 10, None) == 3
 
 
+def test_timed_and_noalloc_argument_checks():
+    """moe_layer_forward_timed needs six event handles; moe_layer_forward_noalloc
+    refuses a T whose workspace exceeds its scratch, before touching a device."""
+    lib = _lib.lib
+    d = ctypes.byref(D())
+    args = [d, 32, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096, None, None, None]
+    need = moe.moe_workspace_size(D(), 32, 0)
+    ev = (ctypes.c_void_p * 6)(*([FAKE] * 5 + [None]))
+    assert lib.moe_layer_forward_timed(*args, FAKE, need, None, None) == 1
+    assert lib.moe_layer_forward_timed(*args, FAKE, need, ev, None) == 1
+    f8 = ctypes.byref(D(weight_dtype=2))
+    assert lib.moe_layer_forward_timed(f8, 32, *args[2:], FAKE, need, ev, None) == 1
+    big = [d, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096, None, None, None, None]
+    assert moe.moe_workspace_size(D(), 65, 0) > moe.MOE_NOALLOC_SCRATCH_BYTES >= moe.moe_workspace_size(D(), 64, 0)
+    assert lib.moe_layer_forward_noalloc(*big) == 3
+    assert lib.moe_layer_forward_noalloc(d, 0, *([None] * 11)) == 0
+    assert lib.moe_layer_forward_noalloc(d, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None,
+                                         None) == 1  # y aliases x
+    assert lib.moe_layer_forward_noalloc(f8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 4096, None, None, None,
+                                         None) == 1
+
+
 def test_binding_requires_device_tensors():
     import torch
     d = moe.make_desc(4096, 14336)

@@ -187,3 +187,24 @@ def test_workload_full_size(wl, n_rows):
     if wl == 3:
         share = counts[:2].sum() / counts.sum()
         assert 0.5 < share < 0.8, share
+
+
+@pytest.mark.parametrize("T,d,F", [(32, 1024, 2048), (1150, 4096, 2048)])
+def test_layer_forward_timed_matches_layer(T, d, F):
+    """moe_layer_forward_timed runs the layer's own launch sequence: the same
+    outputs bit for bit, and its six events in stream order."""
+    inp = mi.make_layer(T, d, F, seed=5, workload=306)
+    desc = moe.make_desc(d, F)
+    x, wg, w1, w3, w2 = (t.cuda() for t in (inp.x, inp.wg, inp.w1, inp.w3, inp.w2))
+    ref = moe.moe_layer_forward(desc, x, wg, w1, w3, w2)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:
+        e.record(stream)
+    got = moe.moe_layer_forward_timed(desc, x, wg, w1, w3, w2, ev)
+    torch.cuda.synchronize()
+    for r, g in zip(ref, got):
+        assert torch.equal(r.cpu(), g.cpu())
+    stages = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+    assert all(s >= 0 for s in stages), stages
+    assert stages[2] > 0 and stages[3] > 0  # the two expert projections
