@@ -181,7 +181,12 @@ moe_status_t moe_rmsnorm(int32_t T, int32_t d, int32_t dtype, const void* h, flo
                          void* x_out, void* stream);
 
 /*
- * The whole layer: router -> permute -> gate/up + SwiGLU -> down -> combine.
+ * The whole layer, y = sum_i G(x)_i E_i(x) with G(x) = Softmax(TopK(x . W_g))
+ * and SwiGLU experts E_i (paper-graph-ui page, section 3.4 "MoE Layer
+ * Formulation": gating, TopK and output equations, and "Expert Network
+ * Structure (SwiGLU)"; xyznot.com reading guide, "Method (with the key
+ * equations)"), computed sparsely: router -> permute -> gate/up + SwiGLU ->
+ * down -> combine, so only the K selected experts run on each token.
  *   x, w_gate, w1, w3, w2   as above
  *   residual                [T, d] or NULL; added to y when present
  *   y                       [T, d] out (may alias residual, must not alias x)
