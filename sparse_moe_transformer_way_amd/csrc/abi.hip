@@ -85,7 +85,8 @@ struct LayerWs {
     int32_t* row_of;
     void* h;
     float* y_perm;
-    float* y_perm_hi;  // second K-partial of the down projection, or nullptr
+    float* y_perm_hi;  // second K-partial of the tiled down projection, or nullptr
+    float* y_tail_hi;  // second K-partial of the down tail pass [n * 64, d], or nullptr
     size_t bytes;
 };
 
@@ -110,6 +111,11 @@ LayerWs carve_layer(const moe_layer_desc_t* d, int32_t T, int32_t tile_m, char* 
     const int parts = (tile_m == 256) ? moe::tiled_down_ksplit(shape_of(d, T)) : 1;
     w.y_perm = reinterpret_cast<float*>(take(parts * P * static_cast<size_t>(d->d_model) * 4));
     w.y_perm_hi = parts == 2 && base != nullptr ? w.y_perm + P * static_cast<size_t>(d->d_model) : nullptr;
+    // and the tail pass cuts K in two with its second partial in a small buffer
+    const bool tail_hi = tile_m == 256 && d->d_ffn % 1024 == 0;
+    w.y_tail_hi = reinterpret_cast<float*>(
+        take(tail_hi ? static_cast<size_t>(d->n_experts) * moe::kTailRows * d->d_model * 4 : 0));
+    if (!tail_hi) w.y_tail_hi = nullptr;
     w.bytes = off;
     return w;
 }
@@ -168,7 +174,7 @@ moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, cons
     if (moe::launch_permute(sh, tile_m, idx, counts, w.offsets, w.row_src, w.row_of, st) != hipSuccess ||
         !record())
         return MOE_ERR_HIP;
-    int parts = 1;
+    int ks_max = 1;
     if (fp8) {
         const auto* q1 = static_cast<const uint8_t*>(ew.w1);
         const auto* q3 = static_cast<const uint8_t*>(ew.w3);
@@ -183,13 +189,13 @@ moe_status_t run_layer(const moe_layer_desc_t* desc, int32_t T, int tile_m, cons
         if (moe::launch_gate_up(sh, tile_m, x, w.row_src, counts, w.offsets, ew.w1, ew.w3, w.h, st) != hipSuccess ||
             !record())
             return MOE_ERR_HIP;
-        if (moe::launch_down(sh, tile_m, w.h, counts, w.offsets, ew.w2, w.y_perm, st, w.y_perm_hi, &parts) !=
-                hipSuccess ||
+        if (moe::launch_down(sh, tile_m, w.h, counts, w.offsets, ew.w2, w.y_perm, st, w.y_perm_hi, w.y_tail_hi,
+                             &ks_max) != hipSuccess ||
             !record())
             return MOE_ERR_HIP;
     }
-    if (moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st, parts == 2 ? w.y_perm_hi : nullptr) !=
-            hipSuccess ||
+    if (moe::launch_combine(sh, w.y_perm, w.row_of, gate, residual, y, st, ks_max == 2 ? w.y_perm_hi : nullptr,
+                            w.y_tail_hi, counts, w.offsets, ks_max) != hipSuccess ||
         !record())
         return MOE_ERR_HIP;
     return MOE_OK;

@@ -44,17 +44,22 @@ __device__ __forceinline__ void combine_store(const float4 (&a)[K], const float 
     }
 }
 
-// Slot s of group c: y_perm row r[s] (+ its second K-part), zero for a dropped
-// slot (r < 0 reads row 0 and discards it).
+// Slot s of group c: y_perm row r[s] (+ its second K-part where the down
+// projection wrote one: hkeep[s] all ones), zero for a dropped slot (r < 0
+// reads row 0 and discards it).
+__device__ __forceinline__ float masked(float v, uint32_t m) { return __uint_as_float(__float_as_uint(v) & m); }
+
 template <int K, bool HI>
 __device__ __forceinline__ void combine_load(const float4* const (&p)[K], const float4* const (&q)[K],
-                                             const uint32_t (&keep)[K], int c, float4 (&a)[K]) {
+                                             const uint32_t (&keep)[K], const uint32_t (&hkeep)[K], int c,
+                                             float4 (&a)[K]) {
 #pragma unroll
     for (int s = 0; s < K; ++s) {
         float4 v = p[s][c];
         if constexpr (HI) {
             const float4 v2 = q[s][c];
-            v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+            v.x += masked(v2.x, hkeep[s]); v.y += masked(v2.y, hkeep[s]);
+            v.z += masked(v2.z, hkeep[s]); v.w += masked(v2.w, hkeep[s]);
         }
         // a bit mask, not a select: the compiler turns a select on a uniform
         // flag into a branch and sinks the loads into it
@@ -70,42 +75,106 @@ __device__ __forceinline__ void combine_load(const float4* const (&p)[K], const 
 // in-place update of a residual stream): neither is marked __restrict__, and
 // each element of the residual is read by the thread that writes it, before
 // that write.
-template <bool BF16, int K, bool HI, bool RES>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ row_of,
-                                                      const float* __restrict__ gate,
-                                                      const void* residual, void* y,
-                                                      int d, const float* __restrict__ y_perm_hi) {
-    constexpr int U = 4;
-    const int t = blockIdx.x;
-    float g[K];
-    uint32_t keep[K];  // all ones for a kept slot, zero for a dropped one
-    const float4* p[K];
-    const float4* q[K];
-#pragma unroll
-    for (int s = 0; s < K; ++s) {
-        const int r = row_of[K * t + s];
-        g[s] = gate[K * t + s];
-        keep[s] = r >= 0 ? 0xffffffffu : 0u;
-        const size_t row = static_cast<size_t>(r < 0 ? 0 : r) * d;
-        p[s] = reinterpret_cast<const float4*>(y_perm + row);
-        q[s] = reinterpret_cast<const float4*>((HI ? y_perm_hi : y_perm) + row);
-    }
+// Token t's d outputs: full passes of U groups per thread with every load
+// issued before the first store, then a plain loop for what is left.
+template <bool BF16, int K, bool HI, bool RES, int U>
+__device__ __forceinline__ void combine_rows(const float4* const (&p)[K], const float4* const (&q)[K],
+                                             const uint32_t (&keep)[K], const uint32_t (&hkeep)[K],
+                                             const float (&g)[K], const void* residual, void* y, int t, int d) {
     const int n4 = d / 4;
     int c = threadIdx.x;
     for (; c + (U - 1) * 256 < n4; c += U * 256) {
         float4 a[U][K];
 #pragma unroll
-        for (int u = 0; u < U; ++u) combine_load<K, HI>(p, q, keep, c + 256 * u, a[u]);
+        for (int u = 0; u < U; ++u) combine_load<K, HI>(p, q, keep, hkeep, c + 256 * u, a[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             combine_store<BF16, K, RES>(a[u], g, residual, y, static_cast<size_t>(t) * d + 4 * (c + 256 * u));
     }
     for (; c < n4; c += 256) {
         float4 a[K];
-        combine_load<K, HI>(p, q, keep, c, a);
+        combine_load<K, HI>(p, q, keep, hkeep, c, a);
         combine_store<BF16, K, RES>(a, g, residual, y, static_cast<size_t>(t) * d + 4 * c);
     }
+}
+
+// The down projection's second K-partials (HI): the tiled kernel's part 1 in
+// y_perm_hi (rows of the tiles it computed, when the plan cut K in two) and the
+// tail pass's part 1 in y_tail_hi (tail row i of expert e at row
+// e * kTailRows + i).  The combine takes the same plan from the same counts.
+struct HiParts {
+    const float* y_perm_hi;
+    const float* y_tail_hi;
+    const int32_t* counts;
+    const int32_t* offsets;
+    int n_exp;
+    int ks_max;
+};
+
+template <bool BF16, int K, bool HI, bool RES>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ gate,
+                                                      const void* residual, void* y,
+                                                      int d, HiParts hp) {
+    constexpr int U = 4;
+    const int t = blockIdx.x;
+    float g[K];
+    uint32_t keep[K];   // all ones for a kept slot, zero for a dropped one
+    uint32_t hkeep[K];  // all ones where the slot's row has a second K-partial
+    const float4* p[K];
+    const float4* q[K];
+    Segments sg;
+    DownPlan plan{1, false};
+    if (HI) {
+        load_segments(hp.offsets, hp.counts, hp.n_exp, sg);
+        plan = down_plan(sg, hp.n_exp, d / kTiledRows, hp.ks_max);
+    }
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+        const int r = row_of[K * t + s];
+        g[s] = gate[K * t + s];
+        keep[s] = r >= 0 ? 0xffffffffu : 0u;
+        const int rr = r < 0 ? 0 : r;
+        const size_t row = static_cast<size_t>(rr) * d;
+        p[s] = reinterpret_cast<const float4*>(y_perm + row);
+        q[s] = p[s];
+        hkeep[s] = 0u;
+        if (HI && (plan.tail || plan.ks == 2)) {
+            // the expert of row rr, its segment start and count, by selects
+            // (indexing the register arrays with a run-time index would put
+            // them in scratch memory)
+            int e = 0, off = sg.off[0], c = sg.cnt[0];
+#pragma unroll
+            for (int j = 1; j < kMaxExperts; ++j) {
+                const bool in = j < hp.n_exp && rr >= sg.off[j];
+                e = in ? j : e;
+                off = in ? sg.off[j] : off;
+                c = in ? sg.cnt[j] : c;
+            }
+            const int rem = c % kTiledRows;
+            const int tail0 = off + c - rem;
+            if (plan.tail && rem > 0 && rem <= kTailRows && rr >= tail0) {
+                if (hp.y_tail_hi != nullptr) {
+                    q[s] = reinterpret_cast<const float4*>(hp.y_tail_hi +
+                                                           static_cast<size_t>(e * kTailRows + rr - tail0) * d);
+                    hkeep[s] = 0xffffffffu;
+                }
+            } else if (plan.ks == 2) {
+                q[s] = reinterpret_cast<const float4*>(hp.y_perm_hi + row);
+                hkeep[s] = 0xffffffffu;
+            }
+        }
+    }
+    // Most tokens have no second partial in any slot (at prefill only the few
+    // tail rows do): those take the plain loop, without the extra loads.
+    uint32_t any = 0;
+#pragma unroll
+    for (int s = 0; s < K; ++s) any |= hkeep[s];
+    if (HI && __builtin_amdgcn_readfirstlane(any) != 0)
+        combine_rows<BF16, K, HI, RES, U>(p, q, keep, hkeep, g, residual, y, t, d);
+    else
+        combine_rows<BF16, K, false, RES, U>(p, q, keep, hkeep, g, residual, y, t, d);
 }
 
 template <bool BF16>
@@ -157,34 +226,38 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
 
 template <bool BF16, bool HI, bool RES>
 static void combine_k(const Shape& s, const float* y_perm, const int32_t* row_of, const float* gate,
-                      const void* residual, void* y, hipStream_t st, const float* y_perm_hi) {
+                      const void* residual, void* y, hipStream_t st, const HiParts& hp) {
     switch (s.K) {
-        case 1: combine_kernel<BF16, 1, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        case 2: combine_kernel<BF16, 2, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        case 3: combine_kernel<BF16, 3, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
-        default: combine_kernel<BF16, 4, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, y_perm_hi); break;
+        case 1: combine_kernel<BF16, 1, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, hp); break;
+        case 2: combine_kernel<BF16, 2, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, hp); break;
+        case 3: combine_kernel<BF16, 3, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, hp); break;
+        default: combine_kernel<BF16, 4, HI, RES><<<s.T, 256, 0, st>>>(y_perm, row_of, gate, residual, y, s.d, hp); break;
     }
 }
 
 template <bool BF16>
 static void combine_dispatch(const Shape& s, const float* y_perm, const int32_t* row_of, const float* gate,
-                             const void* residual, void* y, hipStream_t st, const float* y_perm_hi) {
-    const bool hi = y_perm_hi != nullptr, res = residual != nullptr;
-    if (hi && res) combine_k<BF16, true, true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
-    else if (hi) combine_k<BF16, true, false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
-    else if (res) combine_k<BF16, false, true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
-    else combine_k<BF16, false, false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+                             const void* residual, void* y, hipStream_t st, const HiParts& hp) {
+    const bool hi = hp.y_perm_hi != nullptr || hp.y_tail_hi != nullptr, res = residual != nullptr;
+    if (hi && res) combine_k<BF16, true, true>(s, y_perm, row_of, gate, residual, y, st, hp);
+    else if (hi) combine_k<BF16, true, false>(s, y_perm, row_of, gate, residual, y, st, hp);
+    else if (res) combine_k<BF16, false, true>(s, y_perm, row_of, gate, residual, y, st, hp);
+    else combine_k<BF16, false, false>(s, y_perm, row_of, gate, residual, y, st, hp);
 }
 
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
                           const float* gate, const void* residual, void* y, hipStream_t st,
-                          const float* y_perm_hi) {
+                          const float* y_perm_hi, const float* y_tail_hi, const int32_t* counts,
+                          const int32_t* offsets, int ks_max) {
     static_assert(kMaxTopK == 4, "one combine instance per K");
     if (s.K < 1 || s.K > kMaxTopK) return hipErrorInvalidValue;
+    if ((y_perm_hi != nullptr || y_tail_hi != nullptr) && (counts == nullptr || offsets == nullptr))
+        return hipErrorInvalidValue;
+    const HiParts hp{y_perm_hi, y_tail_hi, counts, offsets, s.n, ks_max};
     if (s.bf16)
-        combine_dispatch<true>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+        combine_dispatch<true>(s, y_perm, row_of, gate, residual, y, st, hp);
     else
-        combine_dispatch<false>(s, y_perm, row_of, gate, residual, y, st, y_perm_hi);
+        combine_dispatch<false>(s, y_perm, row_of, gate, residual, y, st, hp);
     return hipGetLastError();
 }
 

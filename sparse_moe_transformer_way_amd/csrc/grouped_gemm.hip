@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const void* __restrict__ wa, const void* __restrict__ wb, const float* __restrict__ sa,
     const float* __restrict__ sb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert */, int ld_act, int n_src, int P, int topk, int tail_rows,
-    float* __restrict__ out_hi, int tail_parts) {
+    float* __restrict__ out_hi, int plan_ks_max) {
     // Two stage buffers (each 4 wave slices of 8 KB); after the K loop they
     // hold the cross-wave reduction [wave][token block][weight block][lane].
     __shared__ uint4 sb0[4 * kStreamWaveVec];
@@ -216,40 +216,28 @@ __global__ __launch_bounds__(256) void stream_kernel(
 
     const int e = blockIdx.y;
     // K parts (gridDim.z): the down tails may be cut in two, part 1 writing the
-    // second K-partial out_hi that the combine adds
+    // second K-partial of tail row i of expert e to row e * kTailRows + i of
+    // out_hi, which the combine adds
     const int parts = gridDim.z;
     const int part = blockIdx.z;
     int seg = offsets[e];
     // rows [seg, seg_end) may be read and written: the segment, clamped to the buffers
     const int seg_end = min(offsets[e + 1], P);
     int cnt = min(counts[e], seg_end - seg);
-    if (tail_rows > 0) {
-        // Tile-256 layout: only an expert's short tail past its full tiles (the
-        // tiled kernels skip that tile).  Rows of the tail's tile past the
-        // 16-row blocks written below are zeroed here: h padding (gate/up), or
-        // this pass's rows of the tiled kernel's second K-partial (down), which
-        // the combine adds.
+    int tail0 = 0;  // first permuted row of the tail (tail pass only)
+    if (!DUAL && tail_rows > 0) {
+        // Tile-256 layout, down projection: only an expert's short tail past
+        // its full tiles (the tiled kernel skips those tiles), when the plan
+        // that the tiled kernel and the combine also take says so (gridDim.x is
+        // Nw / 64 here; the tiled kernel's weight tiles are Nw / 256).
         const int r = cnt % kTiledRows;
         if (r == 0 || r > tail_rows) return;
-        // the same decision as the tiled kernel's: gridDim.x is Nw / 64 here, the
-        // tiled kernel's weight tiles of 256 rows are Nw / 256, times its K parts
         Segments sg;
         load_segments(offsets, counts, gridDim.y, sg);
-        if (!tail_split_pays(sg, gridDim.y, Nw / kTiledRows * tail_parts)) return;
+        if (!down_plan(sg, gridDim.y, Nw / kTiledRows, plan_ks_max).tail) return;
         seg += cnt - r;
         cnt = r;
-        if (DUAL) {
-            bf16_t* h = static_cast<bf16_t*>(out);
-            const int z0 = seg + ((r + 15) & ~15);
-            const int nz = max(0, seg_end - z0);
-            for (int i = threadIdx.x; i < nz * 4; i += 256)
-                *reinterpret_cast<uint4*>(h + static_cast<size_t>(z0 + (i >> 2)) * Nw + blockIdx.x * 32 +
-                                          (i & 3) * 8) = make_uint4(0, 0, 0, 0);
-        } else if (out_hi != nullptr && parts == 1) {
-            for (int i = threadIdx.x; i < r * 16; i += 256)
-                *reinterpret_cast<uint4*>(out_hi + static_cast<size_t>(seg + (i >> 4)) * Nw + blockIdx.x * 64 +
-                                          (i & 15) * 4) = make_uint4(0, 0, 0, 0);
-        }
+        tail0 = seg;
     }
     if (cnt <= 0) return;
     const int ntb = (cnt + 15) >> 4;
@@ -373,7 +361,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 }
             } else {
                 const int j0 = blockIdx.x * 64;
-                float* yrow = (part ? out_hi : static_cast<float*>(out)) + static_cast<size_t>(p) * Nw;
+                float* yrow = part ? out_hi + static_cast<size_t>(e * kTailRows + (p - tail0)) * Nw
+                                   : static_cast<float*>(out) + static_cast<size_t>(p) * Nw;
 #pragma unroll
                 for (int b = 0; b < kStreamRB; ++b) {
                     if constexpr (FP8)
@@ -508,8 +497,8 @@ hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32
 
 hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
                        const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
-                       float* y_perm_hi, int* n_parts) {
-    if (n_parts != nullptr) *n_parts = 1;
+                       float* y_perm_hi, float* y_tail_hi, int* ks_max) {
+    if (ks_max != nullptr) *ks_max = 1;
     if (!s.bf16) {
         dim3 grid(max_tiles(s, 16), (s.d + 63) / 64);
         f32_kernel<false><<<grid, 256, 0, st>>>(static_cast<const float*>(h), nullptr, counts,
@@ -530,19 +519,19 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
             const size_t P = static_cast<size_t>(pmax_rows(s, 256));
             if (ks == 2 && y_perm_hi != y_perm + P * s.d) ks = 1;
         }
-        if (n_parts != nullptr) *n_parts = ks;
+        if (ks_max != nullptr) *ks_max = ks;
         hipError_t err = launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks, kTailRows);
         if (err != hipSuccess) return err;
         // The tails (a few experts' w2, streamed with at most 64 rows each) run
-        // one block per 64 rows of w2 per expert; with the K split they also
+        // one block per 64 rows of w2 per expert; with a tail buffer they also
         // cut K in two, which doubles the blocks of this latency-bound pass
         // (measured at prefill: 140 -> 90-98 us).
-        const int parts = (ks == 2 && s.F % 1024 == 0) ? 2 : 1;
+        const int parts = (y_tail_hi != nullptr && s.F % 1024 == 0) ? 2 : 1;
         dim3 grid(s.d / 64, s.n, parts);
         stream_kernel<false, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts, offsets,
                                                           w2, nullptr, nullptr, nullptr, y_perm, s.F, s.d, s.F,
                                                           s.T * s.K, pmax_rows(s, 256), s.K, kTailRows,
-                                                          ks == 2 ? y_perm_hi : nullptr, ks);
+                                                          parts == 2 ? y_tail_hi : nullptr, ks);
     }
     return hipGetLastError();
 }

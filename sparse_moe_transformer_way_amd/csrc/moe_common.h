@@ -147,11 +147,21 @@ __device__ __forceinline__ void load_segments(const int32_t* offsets, const int3
     for (int j = 0; j < kMaxExperts; ++j) s.cnt[j] = counts[min(j, n_exp - 1)];
 }
 
-// Whether moving the short tails out of the tiled kernel saves it a round of
-// tiles: ceil(tiles / CUs) drops.  Both the tiled kernel and the streaming
-// tail pass evaluate this from the same device-side counts, so they agree.
-// tiles_per_row_tile: tiles of one 256-row token tile (weight tiles x K parts).
-__device__ __forceinline__ bool tail_split_pays(const Segments& s, int n_exp, int tiles_per_row_tile) {
+// The down projection's plan for one call, taken on the device from the real
+// counts by every kernel that needs it (the tiled kernel, the tail pass and the
+// combine), so that they agree without a host round trip:
+//   ks   K parts of the tiled kernel: 2 only when ks_max allows it and it
+//        lowers the K-weighted round count, ceil(2 t / CUs) / 2 < ceil(t / CUs)
+//        for t tiles (a last round of few tiles is then half as long); each
+//        part writes its own fp32 partial sum, which the combine adds.
+//   tail the experts' short tails (at most kTailRows rows past their full
+//        tiles) go to the streaming pass, when that lowers the round count.
+struct DownPlan {
+    int ks;
+    bool tail;
+};
+
+__device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int n_wt, int ks_max) {
     int with_tail = 0, without = 0;
 #pragma unroll
     for (int e = 0; e < kMaxExperts; ++e) {
@@ -163,9 +173,21 @@ __device__ __forceinline__ bool tail_split_pays(const Segments& s, int n_exp, in
             with_tail += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
         }
     }
-    const int per_round = kComputeUnits;
-    return (with_tail * tiles_per_row_tile + per_round - 1) / per_round <
-           (without * tiles_per_row_tile + per_round - 1) / per_round;
+    DownPlan best{1, false};
+    int best_r = 0;
+    for (int ks = 1; ks <= ks_max; ++ks) {
+        const int per = n_wt * ks;
+        const int r_with = (with_tail * per + kComputeUnits - 1) / kComputeUnits;
+        const int r_without = (without * per + kComputeUnits - 1) / kComputeUnits;
+        const bool tail = r_with < r_without;
+        const int r = tail ? r_with : r_without;
+        // r rounds of K / ks each: compare r / ks across ks (the smaller ks on a tie)
+        if (ks == 1 || r * best.ks < best_r * ks) {
+            best = DownPlan{ks, tail};
+            best_r = r;
+        }
+    }
+    return best;
 }
 
 struct Shape {
@@ -183,12 +205,16 @@ hipError_t launch_permute(const Shape& s, int tile_m, const int32_t* idx, int32_
 hipError_t launch_gate_up(const Shape& s, int tile_m, const void* x, const int32_t* row_src,
                           const int32_t* counts, const int32_t* offsets, const void* w1,
                           const void* w3, void* h, hipStream_t st);
-// With y_perm_hi != nullptr (tile_m 256 only) the K range may be cut in two:
-// the returned count of partial buffers (1 or 2) tells the caller whether
-// y_perm_hi was written; y = y_perm + y_perm_hi then.
+// tile_m 256 only, both optional:
+//   y_perm_hi [P, d]: lets the tiled kernel cut K in two (the plan's ks); part 1
+//     writes it for the rows of the tiles it computes.
+//   y_tail_hi [n * kTailRows, d]: lets the tail pass cut K in two; part 1 writes
+//     tail row i of expert e to row e * kTailRows + i.
+// *ks_max receives the largest K split the plan could take (1 or 2), which the
+// combine needs to take the same plan.
 hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t* counts,
                        const int32_t* offsets, const void* w2, float* y_perm, hipStream_t st,
-                       float* y_perm_hi = nullptr, int* n_parts = nullptr);
+                       float* y_perm_hi = nullptr, float* y_tail_hi = nullptr, int* ks_max = nullptr);
 
 // FP8 (E4M3) expert weights, weight-streaming kernels (tile_m 16, bf16
 // activations): w1/w3 [n, F, d] and w2 [n, d, F] codes with one fp32 scale per
@@ -249,10 +275,13 @@ hipError_t launch_tiled(const Shape& s, bool gate_up, const void* act, const int
 hipError_t launch_tiled_preact(const Shape& s, const void* x, const int32_t* row_src, const int32_t* counts,
                                const int32_t* offsets, const void* w1, const void* w3, float* a, hipStream_t st);
 
-// y_perm_hi (optional): second partial sum of the down projection, added to y_perm.
+// y_perm_hi / y_tail_hi (optional, with the counts, offsets and ks_max given to
+// launch_down): the second K-partials of the down projection, added to y_perm
+// row by row as the down plan wrote them.
 hipError_t launch_combine(const Shape& s, const float* y_perm, const int32_t* row_of,
                           const float* gate, const void* residual, void* y, hipStream_t st,
-                          const float* y_perm_hi = nullptr);
+                          const float* y_perm_hi = nullptr, const float* y_tail_hi = nullptr,
+                          const int32_t* counts = nullptr, const int32_t* offsets = nullptr, int ks_max = 1);
 
 hipError_t launch_rmsnorm(int T, int d, bool bf16, const void* h, float eps, void* x_out,
                           hipStream_t st);

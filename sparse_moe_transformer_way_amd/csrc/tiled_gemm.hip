@@ -52,8 +52,9 @@
 //   * Epilogue stores: gate/up pairs lanes l and l + 32 with a permlane32 swap
 //     so that each lane stores 16 bytes of h; down stages its fp32 rows through
 //     LDS (store_rows_staged) into row-contiguous runs.
-//   * K may be cut into two parts (down projection with few tiles): part s
-//     covers k in [s*K/2, (s+1)*K/2) and writes its own fp32 output buffer.
+//   * K may be cut into two parts (down projection with few tiles, as the
+//     plan of down_plan decides on the device): part s covers k in
+//     [s*K/2, (s+1)*K/2) and writes its own fp32 output buffer.
 #include "moe_common.h"
 
 #include <utility>
@@ -82,7 +83,7 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) | (((row >
 // Token tiles of an expert's segment (length len, padded to kTT, count rows).
 // With tail_rows > 0 a last tile holding at most tail_rows real rows is left
 // to the weight-streaming kernels (it would cost a whole tile here); the
-// kernel only does so when that saves a round of tiles (tail_split_pays).
+// kernel only does so when that saves a round of tiles (down_plan).
 __device__ __forceinline__ int token_tiles(int len, int count, int tail_rows) {
     const int r = count % kTT;
     return (r > 0 && r <= tail_rows) ? count / kTT : len / kTT;
@@ -661,7 +662,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // workgroups exit here)
     Segments sg;
     load_segments(offsets, counts, n_exp, sg);
-    if (tail_rows > 0 && !tail_split_pays(sg, n_exp, n_wt * ksplit)) tail_rows = 0;
+    if (DUAL) {
+        // Gate/up keeps its short tails (as narrow tiles) and its launches pass
+        // no tail_rows, so this test never fires; written this way the
+        // compiler's register allocation of the gate/up kernels has no spills
+        // (with a plain tail_rows = 0 it spilled SGPRs, and VGPRs to scratch in
+        // the pre-activation variant).
+        if (tail_rows > 0 && !down_plan(sg, n_exp, n_wt, ksplit).tail) tail_rows = 0;
+    } else {
+        // down projection: ksplit is the largest K split allowed, the plan picks
+        // the split and whether the short tails go to the streaming pass
+        const DownPlan plan = down_plan(sg, n_exp, n_wt, ksplit);
+        ksplit = plan.ks;
+        if (!plan.tail) tail_rows = 0;
+    }
     TileId t;
     if (!(DUAL ? tile_by_column(sg, n_exp, n_wt, ksplit, tail_rows, t)
                : tile_contiguous(sg, n_exp, n_wt, ksplit, tail_rows, t)))
@@ -879,8 +893,9 @@ bool tiled_fits(const Shape& s) {
 }
 
 int tiled_down_ksplit(const Shape& s) {
-    // Cut the down projection's K in two when its tiles would not fill four
-    // rounds of the 256 CUs (the last, partly empty round then costs less).
+    // Allow the down projection's K to be cut in two when the worst-case tiles
+    // would not fill four rounds of the 256 CUs; down_plan takes the split on
+    // the device only where it shortens the last round.
     const int P = s.T * s.K + s.n * (kTT - 1);
     const int n_tt = (P + kTT - 1) / kTT;
     const int n_wt = s.d / kTW;

@@ -62,32 +62,40 @@ def test_layer_small(dtype, T, d, F):
     check_full(inp, TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
-def down_tail_split_pays(counts, d, F, T, K=2, n=8):
-    """Whether moe_layer_forward's tiled down projection hands the experts'
-    short tails (at most 64 rows past their full 256-row tiles) to the
-    streaming pass: it does when that lowers the number of rounds of 256
-    workgroups, with K cut in two when the tiles fill fewer than four rounds.
-    Returns (K parts, pays)."""
+def down_plan(counts, d, F, T, K=2, n=8):
+    """The down projection's plan that the library takes on the device: the
+    largest K split allowed (2 when the worst-case tiles fill fewer than four
+    rounds of 256 workgroups), then for each split whether the experts' short
+    tails (at most 64 rows past their full 256-row tiles) go to the streaming
+    pass (when that lowers the number of rounds), and the split whose rounds x
+    K per tile is smallest (no split on a tie).  Returns (K parts, tails streamed)."""
     P = T * K + n * 255
     n_tt, n_wt = -(-P // 256), d // 256
-    ks = 2 if (n_tt * n_wt < 4 * 256 and (F // 2) % 256 == 0) else 1
-    per_tile_row = n_wt * ks
+    ks_max = 2 if (n_tt * n_wt < 4 * 256 and (F // 2) % 256 == 0) else 1
     without = sum(-(-c // 256) for c in counts)
     with_tail = sum(c // 256 if 0 < c % 256 <= 64 else -(-c // 256) for c in counts)
-    return ks, -(-with_tail * per_tile_row // 256) < -(-without * per_tile_row // 256)
+    best = None
+    for ks in range(1, ks_max + 1):
+        r_with = -(-with_tail * n_wt * ks // 256)
+        r_without = -(-without * n_wt * ks // 256)
+        tail = r_with < r_without
+        r = min(r_with, r_without)
+        if best is None or r * best[0] < best[2] * ks:
+            best = (ks, tail, r)
+    return best[0], best[1]
 
 
-# d = 4096 with a small F at T = 1150: every expert gets 255-316 rows, so
-# dropping the tail tiles halves the down projection's rounds.  With F = 1536
-# the tail pass runs in one K part and clears its rows of the second partial;
-# with F = 2048 it cuts K in two like the tiled kernel.
+# d = 4096 with a small F at T = 1150: every expert gets 255-316 rows, so the
+# down projection cuts K in two and hands the tails to the streaming pass.
+# With F = 1536 the tail pass runs in one K part (its rows have no second
+# partial); with F = 2048 it cuts K in two into the tail buffer.
 @pytest.mark.parametrize("F,seed", [(1536, 1), (2048, 0)])
 def test_layer_down_tail_pass(F, seed):
     T, d = 1150, 4096
     inp = margin_filtered(mi.make_layer(T, d, F, seed=seed, workload=305))
     counts = np.bincount(oracle.gating(inp.x.float().numpy(), inp.wg.numpy())[1].ravel(), minlength=8)
-    ks, pays = down_tail_split_pays(counts.tolist(), d, F, T)
-    assert ks == 2 and pays, (counts, ks, pays)
+    ks, tail = down_plan(counts.tolist(), d, F, T)
+    assert ks == 2 and tail, (counts, ks, tail)
     err = check_full(inp, TOL_BF16)
     print(f"down tail pass, F={F}: counts {counts.tolist()}, max per-token rel err {err:.3e}")
 
