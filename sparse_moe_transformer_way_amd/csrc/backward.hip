@@ -329,17 +329,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         vt = g.offsets[e] / kTV + vt;  // global v tile (row block of the permuted layout)
     } else {
-        // fixed U x V per expert, K = the expert's rows
+        // fixed U x V per expert, K = the expert's rows, which differ between
+        // experts (rows padded to 256): the v columns of every expert are dealt
+        // over the XCDs, column (e, vt) to XCD (e * nvt + vt) % 8, each with its
+        // nut tiles (which share the column's Y slice) back to back, so every
+        // XCD gets the same mix of experts.  (Contiguous runs gave each XCD one
+        // expert: at prefill four XCDs ran K = 1280 while four ran 1024.)
         const int nvt = g.V / kTV;
-        const int total = g.n_exp * nut * nvt;
-        const int run = (total + 7) >> 3;
-        if (static_cast<int>(blockIdx.x >> 3) >= run) return;
-        const int L = (blockIdx.x & 7) * run + (blockIdx.x >> 3);
-        if (L >= total) return;
-        e = L / (nut * nvt);
-        const int rem = L - e * nut * nvt;
-        ut = rem / nvt;
-        vt = rem - ut * nvt;
+        const int x = blockIdx.x & 7;
+        int i = blockIdx.x >> 3;
+        bool hit = false;
+        for (e = 0; e < g.n_exp; ++e) {
+            const int f = (x - (e * nvt) % 8 + 8) % 8;       // this XCD's first column of expert e
+            const int kk = f < nvt ? (nvt - 1 - f) / 8 + 1 : 0;  // its columns of expert e
+            if (i < kk * nut) {
+                const int col = i / nut;
+                ut = i - col * nut;
+                vt = f + 8 * col;
+                hit = true;
+                break;
+            }
+            i -= kk * nut;
+        }
+        if (!hit) return;
         kbeg = g.offsets[e];
         klen = g.offsets[e + 1] - kbeg;
     }
@@ -825,6 +837,8 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
 
     const int vmax = (P + kTV - 1) / kTV;  // worst-case row tiles
     auto grid8 = [](long long tiles) { return static_cast<int>((tiles + 7) / 8 * 8); };
+    // weight-gradient products: an XCD takes ceil(nvt / 8) columns of nut tiles of each expert
+    auto dw_grid = [&](int nut, int nvt) { return static_cast<int>(8LL * n * ((nvt + 7) / 8) * nut); };
 
     // 1. a = [a1 | a3] in fp32: the forward pass's tiled gate/up kernel with a
     //    pre-activation epilogue (same rows, same tile order)
@@ -859,9 +873,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.U = F; g.V = d; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = dw2; g.c1 = dw2; g.c_estride = static_cast<int64_t>(d) * F; g.ldc = F; g.csplit = 0; g.P = P;
     g.ksplit = 1;
-    if ((err = launch_gemm<true, true, kEpiDw, false>(
-             g, grid8(static_cast<long long>(n) * (F / kTU) * (d / kTV)), st)) != hipSuccess)
-        return err;
+    if ((err = launch_gemm<true, true, kEpiDw, false>(g, dw_grid(F / kTU, d / kTV), st)) != hipSuccess) return err;
 
     // 5. dw1/dw3[e][f][j] = sum_p da[p][f'] xp[p][j]: u = j, v = f' (f' >= F: dw3)
     g = GemmArgs{};
@@ -870,8 +882,7 @@ hipError_t launch_layer_backward(const Shape& s, const void* x, const float* wg,
     g.U = d; g.V = 2 * F; g.K = 0; g.offsets = w.offsets; g.n_exp = n;
     g.c0 = dw1; g.c1 = dw3; g.c_estride = static_cast<int64_t>(F) * d; g.ldc = d; g.csplit = F; g.P = P;
     g.ksplit = 1;
-    if ((err = launch_gemm<true, true, kEpiDw, false>(
-             g, grid8(static_cast<long long>(n) * (d / kTU) * (2 * F / kTV)), st)) != hipSuccess)
+    if ((err = launch_gemm<true, true, kEpiDw, false>(g, dw_grid(d / kTU, 2 * F / kTV), st)) != hipSuccess)
         return err;
 
     // router gradient, dx, dW_g
