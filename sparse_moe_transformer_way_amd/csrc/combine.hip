@@ -68,15 +68,9 @@ __device__ __forceinline__ void combine_load(const float4* const (&p)[K], const 
     }
 }
 
-// One block of 256 threads per token.  Full passes take U groups per thread
-// with every load issued before the first store (a decode row, d = 4096, is
-// one pass), then a plain loop takes what is left.  HI: y_perm has a second
-// K-part to add; RES: a residual is added.  residual may be y itself (the
-// in-place update of a residual stream): neither is marked __restrict__, and
-// each element of the residual is read by the thread that writes it, before
-// that write.
 // Token t's d outputs: full passes of U groups per thread with every load
-// issued before the first store, then a plain loop for what is left.
+// issued before the first store (a decode row, d = 4096, is one pass), then a
+// plain loop for what is left.
 template <bool BF16, int K, bool HI, bool RES, int U>
 __device__ __forceinline__ void combine_rows(const float4* const (&p)[K], const float4* const (&q)[K],
                                              const uint32_t (&keep)[K], const uint32_t (&hkeep)[K],
@@ -111,6 +105,11 @@ struct HiParts {
     int ks_max;
 };
 
+// One block of 256 threads per token.  HI: the layer's down projection may
+// have written second K-partials; RES: a residual is added.  residual may be
+// y itself (the in-place update of a residual stream): neither is marked
+// __restrict__, and each element of the residual is read by the thread that
+// writes it, before that write.
 template <bool BF16, int K, bool HI, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
