@@ -331,26 +331,28 @@ __device__ __forceinline__ void mfma_narrow(const u32x4_t (&f)[2 * (2 + TB)], f3
 }
 
 // 4 * TB MFMAs, each followed by its share of the stage's fragment reads
-// (READ) and of NC copies.
-template <int TB, bool READ, int NC, int U>
+// (READ) and of NC copies (FRONT: the copies over the first half of the
+// MFMAs, as the full tiles of the down projection do).
+template <int TB, bool READ, int NC, int U, bool FRONT = false>
 __device__ __forceinline__ void sched_narrow_unit() {
     constexpr int kM = 4 * TB;
     constexpr int kR = (U + 1) * 2 * (2 + TB) / kM - U * 2 * (2 + TB) / kM;
-    constexpr int kC = (U + 1) * NC / kM - U * NC / kM;
+    constexpr int kMc = FRONT ? kM / 2 : kM;
+    constexpr int kC = U < kMc ? (U + 1) * NC / kMc - U * NC / kMc : 0;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (READ && kR > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kR, 0);
     if constexpr (kC > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, kC, 0);
 }
 
-template <int TB, bool READ, int NC, int... U>
+template <int TB, bool READ, int NC, bool FRONT, int... U>
 __device__ __forceinline__ void sched_narrow_seq(std::integer_sequence<int, U...>) {
-    (sched_narrow_unit<TB, READ, NC, U>(), ...);
+    (sched_narrow_unit<TB, READ, NC, U, FRONT>(), ...);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int TB, bool READ, int NC>
+template <int TB, bool READ, int NC, bool FRONT = false>
 __device__ __forceinline__ void sched_narrow() {
-    sched_narrow_seq<TB, READ, NC>(std::make_integer_sequence<int, 4 * TB>{});
+    sched_narrow_seq<TB, READ, NC, FRONT>(std::make_integer_sequence<int, 4 * TB>{});
 }
 
 // uint4 of one 64-k block of a narrow tile (weight rows, then its token rows)
@@ -388,7 +390,7 @@ __device__ __forceinline__ void narrow_step(const TileCtx& c, const NarrowCtx& n
     }
     if (NEXT) read_narrow<TB>(n, nxt, 0, f0);
     mfma_narrow<TB>(f1, acc);
-    sched_narrow<TB, NEXT, COPY ? SUB * (8 + TB) : 0>();
+    sched_narrow<TB, NEXT, COPY ? SUB * (8 + TB) : 0, !DUAL>();  // the down projection front-loads its copies
 }
 
 // The whole narrow tile: copies, K loop, epilogue.  Gate/up also writes zeros
