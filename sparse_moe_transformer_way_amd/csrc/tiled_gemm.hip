@@ -120,7 +120,7 @@ struct TileCtx {
     int dma;                      // uint4 offset of this wave's first copy group in a buffer
     int rd[4];                    // per (half of the block, k16 half): fragment index in weight block 0
     int rdt;                      // uint4 distance from weight block 0 to token block 0
-    uint32_t pfo;                 // down: lane byte offset of its prefetch, weight row `lane`
+    uint32_t pfo;                 // lane byte offset of its prefetch, weight row `lane`
 };
 
 // Weight block j of this wave (uint4 offset from block 0).  Gate/up: blocks 0,
@@ -195,11 +195,14 @@ __device__ __forceinline__ void sched_half() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Down projection: at the end of block kb each wave also loads one dword from
-// each of its 64 w2 rows in block kb + 3 (a 128-byte line per row), which
-// brings that block's weight lines into L2 a block before they are copied.
-// w2 and h do not fit the MALL together, so the down projection's copies wait
-// on HBM; gate/up (its gathered x fits the MALL) gains nothing from it.
+// Weight-line prefetch: at the end of block kb each wave also loads one dword
+// from each of its 64 weight rows in block kb + 3 (a 128-byte line per row),
+// which brings that block's weight lines into L2 a block before they are
+// copied.  w2 and h do not fit the MALL together, so every down tile waits on
+// HBM for its copies and prefetches.  In gate/up (its gathered x fits the
+// MALL) only the first token tile of each weight column prefetches: it is the
+// one that reads the column's weights from HBM, the later tiles of the column
+// find them in L2, and a prefetch there is only one more load in flight.
 constexpr int kPrefetchAhead = 3;
 template <bool DUAL>
 constexpr bool kPrefetch = !DUAL;
@@ -211,7 +214,7 @@ constexpr bool kPrefetch = !DUAL;
 //                and every wave has read all of `cur` - then (COPY) copy block
 //                kb+2 into `cur` and read block kb+1's first half into f0 from
 //                `nxt`; MFMAs on f1.
-//   then       : (PF, down only) the prefetch of block kb + 3 into pf, after a
+//   then       : (PF, prefetching tiles) the prefetch of block kb + 3 into pf, after a
 //                scheduling fence, so it is the wave's last memory operation.
 // The barrier waits for block kb+1's copies, issued a block earlier: for every
 // outstanding vector-memory operation (vmcnt 0), or (PFWAIT) for all but the
@@ -219,11 +222,12 @@ constexpr bool kPrefetch = !DUAL;
 // written two blocks after its load (the load of block kb - 2 has completed by
 // block kb's barrier); CONSUME marks it as read there, so the compiler keeps
 // the load and never has to wait for it.
-template <bool DUAL, bool ACTIVE, bool COPY, bool NEXT, bool PFWAIT = false, bool CONSUME = false, bool PF = false>
+template <bool DUAL, bool ACTIVE, bool COPY, bool NEXT, bool PFWAIT = false, bool CONSUME = false, bool PF = false,
+          bool PFON = kPrefetch<DUAL>>
 __device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__ cur, const uint4* __restrict__ nxt,
                                            int kb, int nb, Frag16& f0, Frag16& f1, f32x16_t (&acc)[4][4],
                                            uint32_t& pf) {
-    constexpr bool kPf = kPrefetch<DUAL>;
+    constexpr bool kPf = PFON;
     if (ACTIVE) {
         read_half<DUAL>(c, cur, 1, f1);
         mfma_half(f0, acc);
@@ -250,24 +254,24 @@ __device__ __forceinline__ void block_step(const TileCtx& c, uint4* __restrict__
 // and 1 are being copied into b0 and b1, the weights of both first, then the
 // tokens of block 0, then those of block 1.  Blocks 0 and 1 are peeled: no
 // prefetch is outstanding at block 0's barrier, and none is consumed before
-// block 2.
-template <bool DUAL, bool ACTIVE>
+// block 2.  PFON: this tile prefetches its weight lines.
+template <bool DUAL, bool ACTIVE, bool PFON = kPrefetch<DUAL>>
 __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1, int nb, f32x16_t (&acc)[4][4]) {
     block_barrier<kCopies / 2>();  // block 0 has landed (block 1's token copies may not have)
     Frag16 f0, f1;
     uint32_t pf0 = 0, pf1 = 0;  // prefetch registers of the even and the odd blocks
     if (ACTIVE) read_half<DUAL>(c, b0, 0, f0);
-    block_step<DUAL, ACTIVE, true, true, false, false, true>(c, b0, b1, 0, nb, f0, f1, acc, pf0);
-    block_step<DUAL, ACTIVE, true, true, true, false, true>(c, b1, b0, 1, nb, f0, f1, acc, pf1);
+    block_step<DUAL, ACTIVE, true, true, false, false, true, PFON>(c, b0, b1, 0, nb, f0, f1, acc, pf0);
+    block_step<DUAL, ACTIVE, true, true, true, false, true, PFON>(c, b1, b0, 1, nb, f0, f1, acc, pf1);
     int kb = 2;
     while (kb < nb - 2) {
-        block_step<DUAL, ACTIVE, true, true, true, true, true>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
-        block_step<DUAL, ACTIVE, true, true, true, true, true>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
+        block_step<DUAL, ACTIVE, true, true, true, true, true, PFON>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
+        block_step<DUAL, ACTIVE, true, true, true, true, true, PFON>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
         kb += 2;
     }
-    block_step<DUAL, ACTIVE, false, true, true, true, false>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
-    block_step<DUAL, ACTIVE, false, false>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
-    if (kPrefetch<DUAL>) asm volatile("" ::"v"(pf1));
+    block_step<DUAL, ACTIVE, false, true, true, true, false, PFON>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
+    block_step<DUAL, ACTIVE, false, false, false, false, false, PFON>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
+    if (PFON) asm volatile("" ::"v"(pf1));
 }
 
 // ---- Narrow tiles.  An expert's last token tile often holds few real rows
@@ -802,10 +806,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
     // A wave whose 128 token rows are all padding skips its reads and MFMAs.
-    if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0)
-        main_loop<DUAL, true>(c, b0, b1, nb, acc);
-    else
-        main_loop<DUAL, false>(c, b0, b1, nb, acc);
+    // In gate/up the first token tile of a weight column prefetches its lines.
+    const bool leader = DUAL && ttl == 0;
+    if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0) {
+        if (leader) main_loop<DUAL, true, true>(c, b0, b1, nb, acc);
+        else main_loop<DUAL, true>(c, b0, b1, nb, acc);
+    } else {
+        if (leader) main_loop<DUAL, false, true>(c, b0, b1, nb, acc);
+        else main_loop<DUAL, false>(c, b0, b1, nb, acc);
+    }
 
     // ---- epilogue.  32x32 C layout: lane l holds token column l%32 and weight
     // rows 8*(q/4) + 4*(l/32) + q%4 of each block, q = 0..15.
