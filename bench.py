@@ -71,6 +71,9 @@ def parse_args():
                     help="decode only: leave out the prefill block of the default run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--vs-library", action="store_true",
+                    help="only compare the tiled expert projections with hipBLASLt (torch.bmm) on the "
+                         "same grouped shapes, with exactly balanced routing")
     return ap.parse_args()
 
 
@@ -103,6 +106,93 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "copies": 5}))
+
+
+def vs_library(args):
+    """The two expert projections at prefill and stack sizes (T = 4096, 8192; d = 4096,
+    F = 14336, 8 experts, top-2) with exactly balanced routing, T*K/8 rows per expert:
+    moe_expert_gate_up / moe_expert_down (tile 256) against hipBLASLt's batched GEMM
+    (torch.bmm, one batch per expert, contiguous operands) on the same shapes.  The
+    library GEMMs compute less: no gather of x rows, no SwiGLU (gate/up writes both
+    2F-wide products), no ragged segments.  The chip's clock ramps up over the first
+    tens of milliseconds of load, so each kernel first runs for half a second, and the
+    four kernels are then timed in three interleaved rounds (median over all calls).
+    Prints one JSON line."""
+    import torch
+    import sparse_moe_transformer_way_amd as moe
+
+    dev = torch.device("cuda")
+    d, F, n, K = 4096, 14336, 8, 2
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def warm(fn, seconds=0.5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+
+    def timed(fn):
+        ev = events(args.steps + 1, stream)
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            ev[s].record(stream)
+            fn()
+        ev[args.steps].record(stream)
+        torch.cuda.synchronize()
+        return [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+
+    def randn(*shape):
+        return (torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+
+    rows = []
+    for T in (4096, 8192):
+        M = T * K // n
+        desc = moe.make_desc(d, F, n, K, dtype=torch.bfloat16)
+        x = randn(T, d)
+        w1, w3, w2 = randn(n, F, d), randn(n, F, d), randn(n, d, F)
+        counts = torch.full((n,), M, dtype=torch.int32, device=dev)
+        offsets = torch.arange(0, n * M + 1, M, dtype=torch.int32, device=dev)
+        # expert e takes the assignments t*K + k with (t*K + k) % n == e, in token order
+        # (segments of M rows, a multiple of the tile: no padding rows inside them)
+        P = moe.moe_max_permuted_rows(desc, T, 256)
+        a = torch.arange(T * K, device=dev, dtype=torch.int32)
+        row_src = torch.full((P,), -1, dtype=torch.int32, device=dev)
+        row_src[:n * M] = torch.cat([a[a % n == e] for e in range(n)])
+        h = torch.empty((P, F), dtype=torch.bfloat16, device=dev)
+        y_perm = torch.empty((P, d), dtype=torch.float32, device=dev)
+        xe = x[(row_src[:n * M] // K).long()].view(n, M, d).contiguous()
+        w13t = torch.cat([w1, w3], dim=1).transpose(1, 2).contiguous()  # [n, d, 2F]
+        w2t = w2.transpose(1, 2).contiguous()                            # [n, F, d]
+        he = randn(n, M, F)
+        fns = {
+            "ours_gate_up": lambda: moe.moe_expert_gate_up(desc, T, 256, x, row_src, counts, offsets, w1, w3, h,
+                                                           stream=stream),
+            "ours_down": lambda: moe.moe_expert_down(desc, T, 256, h, counts, offsets, w2, y_perm, stream=stream),
+            "lib_gate_up": lambda: torch.bmm(xe, w13t),
+            "lib_down": lambda: torch.bmm(he, w2t),
+        }
+        for fn in fns.values():
+            warm(fn)
+        times = {k: [] for k in fns}
+        for _ in range(3):
+            for k, fn in fns.items():
+                times[k] += timed(fn)
+        med = {k: statistics.median(v) for k, v in times.items()}
+        for name, flop in (("gate_up", 4.0 * n * M * d * F), ("down", 2.0 * n * M * F * d)):
+            ours, lib = med["ours_" + name], med["lib_" + name]
+            rows.append({"T": T, "rows_per_expert": M, "projection": name,
+                         "ours_ms": round(ours, 4), "hipblaslt_bmm_ms": round(lib, 4),
+                         "ours_mfma_frac": round(flop / ours / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "hipblaslt_mfma_frac": round(flop / lib / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)})
+        del fns, x, w1, w3, w2, h, y_perm, xe, w13t, w2t, he
+        torch.cuda.empty_cache()
+    print(json.dumps({"comparison": "tiled expert projections vs hipBLASLt batched GEMM (torch.bmm), "
+                      "balanced routing, median of per-call HIP events over three interleaved rounds",
+                      "steps_per_round": args.steps, "rows": rows}), flush=True)
 
 
 def host_facts() -> dict:
@@ -543,6 +633,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.vs_library:
+        vs_library(args)
         return
 
     import moe_inputs as mi
