@@ -18,8 +18,10 @@
 //     with the LDS destination bit (no register staging), 8 rows x 128 bytes
 //     per wave instruction, so every request covers a whole 128-byte line
 //     (measured on MI355X: half-line copies of 32-k stages issued twice the L2
-//     requests and ran the kernels 8-11% slower).  Two buffers: block kb+2 is
-//     copied while block kb+1 lands and block kb is consumed.
+//     requests and ran the kernels 8-11% slower).  Gate/up: two buffers, block
+//     kb+2 is copied while block kb+1 lands and block kb is consumed.  Down:
+//     two weight and three token buffers of 32 KB (all of the LDS), so the
+//     token rows of block kb+3 are copied while block kb is consumed.
 //   * A block is consumed as two 32-k stages of 32 MFMAs; each stage's 16
 //     fragments are read into a second register set under the previous
 //     stage's MFMAs, one read per two MFMAs; the copies of a block go out
@@ -46,7 +48,7 @@
 //   * An expert's last token tile with at most 128 real rows runs as a narrow
 //     tile (narrow_tile): 64 or 128 token rows, the weight rows split over the
 //     four waves.  A 64-row narrow tile moves 128 k per buffer (two 64-k
-//     blocks of 40 KB), which is why each buffer is 80 KB.
+//     blocks of 40 KB), so its two buffers take 80 KB each.
 //   * Padding rows of a token tile copy a real row (gate/up) or the padded rows
 //     of h (down).  Gate/up writes zeros for them into h; down writes whatever
 //     they sum to (y_perm rows past an expert's count are unspecified).
@@ -269,9 +271,120 @@ __device__ __forceinline__ void main_loop(const TileCtx& c, uint4* b0, uint4* b1
         block_step<DUAL, ACTIVE, true, true, true, true, true, PFON>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
         kb += 2;
     }
-    block_step<DUAL, ACTIVE, false, true, true, true, false, PFON>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
+    // the barrier of block nb - 2 waits for everything: the last prefetch is
+    // consumed only after the loop, so the compiler may sink it past that
+    // barrier (the weights are restrict-qualified)
+    block_step<DUAL, ACTIVE, false, true, false, true, false, PFON>(c, b0, b1, kb, nb, f0, f1, acc, pf0);
     block_step<DUAL, ACTIVE, false, false, false, false, false, PFON>(c, b1, b0, kb + 1, nb, f0, f1, acc, pf1);
     if (PFON) asm volatile("" ::"v"(pf1));
+}
+
+// ---- Down projection with three token buffers.  LDS (160 KB) holds two
+// weight buffers W0, W1 and three token buffers T0-T2 of 32 KB each; block kb
+// takes W[kb % 2] and T[kb % 3].  At block kb's barrier both of its buffers
+// are free: the weights of block kb + 2 and the tokens of block kb + 3 are
+// copied into them, so the token rows (h, from HBM) have two blocks to land
+// and the weight rows one (their lines were brought into L2 by the prefetch).
+constexpr int kHalfVec = kTW * kChunks;  // uint4 of one 32 KB buffer (256 rows of one operand)
+static_assert(5 * kHalfVec <= 2 * kLdsVec, "two weight and three token buffers fit the LDS");
+
+__device__ __forceinline__ void read_half_t3(const TileCtx& c, const uint4* __restrict__ wbuf,
+                                             const uint4* __restrict__ tbuf, int s, Frag16& f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4* pw = wbuf + c.rd[2 * s + h];
+        const uint4* pt = tbuf + (c.rdt - kHalfVec) + c.rd[2 * s + h];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[8 * h + j] = __builtin_bit_cast(u32x4_t, pw[wblk<false>(j)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[8 * h + 4 + i] = __builtin_bit_cast(u32x4_t, pt[i * 32 * kChunks]);
+    }
+}
+
+// token copy jj (8-row group) of the block at k0 into the token buffer tbuf
+__device__ __forceinline__ void copy_t_t3(const TileCtx& c, uint4* __restrict__ tbuf, int k0, int jj) {
+    // address-space conversion needs a C-style cast
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.tres, (lptr_t)(tbuf + c.dma + jj * kGroupVec), 16,
+                                             c.to[(jj >> 1) & 1], jj * c.tstride + 2 * k0, 0, 0);
+}
+
+// Block kb: as block_step, with the barrier leaving the N youngest vector-
+// memory operations in flight, then (WCOPY) the weight copies of block kb + 2
+// into wcur and (TCOPY) the token copies of block kb + 3 into tcur.
+template <bool ACTIVE, bool WCOPY, bool TCOPY, bool NEXT, int N, bool CONSUME, bool PF>
+__device__ __forceinline__ void block_step_t3(const TileCtx& c, uint4* __restrict__ wcur,
+                                              const uint4* __restrict__ wnxt, uint4* __restrict__ tcur,
+                                              const uint4* __restrict__ tnxt, int kb, int nb, Frag16& f0,
+                                              Frag16& f1, f32x16_t (&acc)[4][4], uint32_t& pf) {
+    if (ACTIVE) {
+        read_half_t3(c, wcur, tcur, 1, f1);
+        mfma_half(f0, acc);
+        sched_half<true, false>();
+    }
+    if (NEXT) block_barrier<N>();
+    if (CONSUME) asm volatile("" ::"v"(pf));
+    if (WCOPY) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) copy_one<false>(c, wcur, (kb + 2) * kBK, j);
+    }
+    if (TCOPY) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) copy_t_t3(c, tcur, (kb + 3) * kBK, jj);
+    }
+    if (ACTIVE) {
+        if (NEXT) read_half_t3(c, wnxt, tnxt, 0, f0);
+        mfma_half(f1, acc);
+        sched_half<NEXT, WCOPY, false>();
+    }
+    if (PF) {
+        __builtin_amdgcn_sched_barrier(0);
+        pf = __builtin_amdgcn_raw_buffer_load_b32(c.wres, c.pfo, 2 * min(kb + kPrefetchAhead, nb - 1) * kBK, 0);
+    }
+}
+
+// The K loop of a full down tile (nb a multiple of 4, >= 4).  Before it: the
+// weight copies of blocks 0 and 1 into W0 and W1.  After the token copies of
+// blocks 0-2 a prefetch (of block 2's weight lines) goes out too, so that at
+// every barrier of the loop the youngest 9 operations (8 token copies and a
+// prefetch) are the ones that may stay in flight.
+template <bool ACTIVE>
+__device__ __forceinline__ void main_loop_t3(const TileCtx& c, uint4* lds, int nb, f32x16_t (&acc)[4][4]) {
+    uint4* const W0 = lds;
+    uint4* const W1 = lds + kHalfVec;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) copy_t_t3(c, lds + 2 * kHalfVec, 0, jj);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) copy_t_t3(c, lds + 3 * kHalfVec, kBK, jj);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) copy_t_t3(c, lds + 4 * kHalfVec, 2 * kBK, jj);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t pf0 = 0;  // prefetch registers of the even and the odd blocks
+    uint32_t pf1 = __builtin_amdgcn_raw_buffer_load_b32(c.wres, c.pfo, 2 * min(2, nb - 1) * kBK, 0);
+    block_barrier<17>();  // block 0 (and the weights of block 1) have landed
+    Frag16 f0, f1;
+    uint4* ta = lds + 2 * kHalfVec;  // T[kb % 3]
+    uint4* tb = lds + 3 * kHalfVec;  // T[(kb + 1) % 3]
+    uint4* tc = lds + 4 * kHalfVec;  // T[(kb + 2) % 3]
+    if (ACTIVE) read_half_t3(c, W0, ta, 0, f0);
+    int kb = 0;
+    while (kb <= nb - 5) {
+        block_step_t3<ACTIVE, true, true, true, 9, true, true>(c, W0, W1, ta, tb, kb, nb, f0, f1, acc, pf0);
+        block_step_t3<ACTIVE, true, true, true, 9, true, true>(c, W1, W0, tb, tc, kb + 1, nb, f0, f1, acc, pf1);
+        uint4* const t = ta;
+        ta = tc;
+        tc = tb;
+        tb = t;
+        kb += 2;
+    }
+    // kb = nb - 4: the last token copies (block nb - 1), then the last weight
+    // copies (with no prefetch: its block is being copied), then the barrier
+    // of block nb - 2 waits for everything.  A prefetch consumed only after
+    // the loop could be sunk past that barrier by the compiler (the weights
+    // are restrict-qualified), so none is left in flight there.
+    block_step_t3<ACTIVE, true, true, true, 9, true, true>(c, W0, W1, ta, tb, kb, nb, f0, f1, acc, pf0);
+    block_step_t3<ACTIVE, true, false, true, 9, true, false>(c, W1, W0, tb, tc, kb + 1, nb, f0, f1, acc, pf1);
+    block_step_t3<ACTIVE, false, false, true, 0, true, false>(c, W0, W1, tc, ta, kb + 2, nb, f0, f1, acc, pf0);
+    block_step_t3<ACTIVE, false, false, false, 0, false, false>(c, W1, W0, ta, tb, kb + 3, nb, f0, f1, acc, pf1);
 }
 
 // ---- Narrow tiles.  An expert's last token tile often holds few real rows
@@ -670,8 +783,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ wa, const bf16_t* __restrict__ wb, void* __restrict__ out,
     int Kdim, int Nw /* weight rows per expert (F or d) */, int ld_act, int n_wt,
     int ld_out, int n_src, int P, int ksplit, size_t split_stride, int n_exp, int topk, int tail_rows) {
-    __shared__ uint4 b0[kLdsVec];
-    __shared__ uint4 b1[kLdsVec];
+    __shared__ uint4 lds[2 * kLdsVec];
+    uint4* const b0 = lds;
+    uint4* const b1 = lds + kLdsVec;
 
     // ---- tile of this workgroup (the grid covers the worst case; spare
     // workgroups exit here)
@@ -762,7 +876,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b0, 0, j);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, b1, kBK, j);
+    for (int j = 0; j < 8; ++j) copy_one<DUAL>(c, DUAL ? b1 : lds + kHalfVec, kBK, j);
     {
         if (DUAL) {
             c.tres = make_rsrc(act + kbase);
@@ -801,19 +915,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
 
     const int nb = kpart / kBK;  // a multiple of 4, >= 4 (K parts are multiples of 256)
+    if constexpr (DUAL) {
 #pragma unroll
-    for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b0, 0, j);
+        for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b0, 0, j);
 #pragma unroll
-    for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
+        for (int j = 8; j < kCopies; ++j) copy_one<DUAL>(c, b1, kBK, j);
+    }
     // A wave whose 128 token rows are all padding skips its reads and MFMAs.
     // In gate/up the first token tile of a weight column prefetches its lines.
     const bool leader = DUAL && ttl == 0;
-    if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0) {
-        if (leader) main_loop<DUAL, true, true>(c, b0, b1, nb, acc);
-        else main_loop<DUAL, true>(c, b0, b1, nb, acc);
+    if constexpr (!DUAL) {
+        if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0)
+            main_loop_t3<true>(c, lds, nb, acc);
+        else
+            main_loop_t3<false>(c, lds, nb, acc);
     } else {
-        if (leader) main_loop<DUAL, false, true>(c, b0, b1, nb, acc);
-        else main_loop<DUAL, false>(c, b0, b1, nb, acc);
+        if (__builtin_amdgcn_readfirstlane(valid > wave_t * 128 ? 1 : 0) != 0) {
+            if (leader) main_loop<DUAL, true, true>(c, b0, b1, nb, acc);
+            else main_loop<DUAL, true>(c, b0, b1, nb, acc);
+        } else {
+            if (leader) main_loop<DUAL, false, true>(c, b0, b1, nb, acc);
+            else main_loop<DUAL, false>(c, b0, b1, nb, acc);
+        }
     }
 
     // ---- epilogue.  32x32 C layout: lane l holds token column l%32 and weight

@@ -1,16 +1,18 @@
 """The hand-counted vector-memory waits of the tiled MFMA kernels hold in the
 code the compiler emits (gfx950 assembly, no GPU needed).
 
-Where a tile prefetches its weight lines into L2, the barrier before the second
-stage of a block waits with vmcnt(1): vector-memory operations of a wave
-complete in issue order, and the one operation allowed to stay in flight is
-meant to be that prefetch, issued after the block's LDS copies.  That is exact
-only while the prefetch is the wave's last vector-memory instruction before the
-barrier, on the fall-through path and on a loop's back edge alike.  The loaded
-row pointers are restrict-qualified, so the compiler is free to move such a
-load (a variant that staged token rows through registers had its loads sunk
-past a barrier that way).  This test compiles tiled_gemm.hip to assembly and
-checks the order in every tiled kernel.
+Vector-memory operations of a wave complete in issue order, so a barrier that
+waits with vmcnt(N) leaves exactly the N youngest in flight.  The kernels count
+those on purpose: LDS copies of later blocks (buffer loads with the LDS bit)
+and, last, the L2 prefetch of a block's weight lines (one dword into a
+register).  That is exact only while the emitted order is the written one, on
+the fall-through path and on a loop's back edge alike.  The loaded row pointers
+are restrict-qualified, so the compiler is free to move a plain load (a variant
+that staged token rows through registers had its loads sunk past a barrier
+that way).  This test compiles tiled_gemm.hip to assembly and checks, before
+every counted barrier (vmcnt(N) with N > 0, then s_barrier) of every tiled
+kernel: the N youngest vector-memory instructions are LDS copies, except that
+the youngest may be the prefetch, and for vmcnt(1) it must be.
 """
 import os
 import re
@@ -24,7 +26,8 @@ sys.path.insert(0, os.path.join(ROOT, "sparse_moe_transformer_way_amd"))
 import build as B  # noqa: E402
 
 VMEM = re.compile(r"^\s*(buffer|global|flat)_(load|store|atomic)\w*")
-PREFETCH = re.compile(r"^\s*buffer_load_dword\s+v\d+,")  # one dword into a VGPR, no LDS bit
+PREFETCH = re.compile(r"^\s*buffer_load_dword\s+v\d+,(?!.*\blds\b)")  # one dword into a VGPR, no LDS bit
+LDS_COPY = re.compile(r"^\s*buffer_load_dword\w*\s.*\blds\s*$")       # a copy straight into LDS
 LABEL = re.compile(r"^(\.LBB\w+):")
 BRANCH = re.compile(r"^\s*s_cbranch_\w+\s+(\.LBB\w+)|^\s*s_branch\s+(\.LBB\w+)")
 
@@ -57,34 +60,43 @@ def tiled_asm(tmp_path_factory):
     return out.read_text()
 
 
+def _window_ok(window, n):
+    """The n youngest vector-memory instructions (oldest first): LDS copies,
+    the youngest possibly the prefetch (and for n == 1 necessarily)."""
+    if len(window) < n:
+        return False
+    *older, youngest = window[-n:]
+    if n == 1:
+        return PREFETCH.match(youngest) is not None
+    return all(LDS_COPY.match(w) for w in older) and (LDS_COPY.match(youngest) or PREFETCH.match(youngest))
+
+
 def _check(lines, headers):
-    """Returns (number of vmcnt(1) barriers, violations)."""
+    """Returns (number of counted barriers, violations)."""
     labels = {LABEL.match(l).group(1): i for i, l in enumerate(lines) if LABEL.match(l)}
-    last_at = []  # line index -> latest vector-memory instruction before it, in textual order
-    last_vmem = None
+    before = []  # line index -> vector-memory instructions before it, in textual order
+    seen = []
     for l in lines:
-        last_at.append(last_vmem)
+        before.append(list(seen[-64:]))
         if VMEM.match(l):
-            last_vmem = l.strip()
+            seen.append(l.strip())
     bad, count = [], 0
     for i, l in enumerate(lines):
-        last_vmem = last_at[i]
-        if re.match(r"^\s*s_waitcnt\b.*\bvmcnt\(1\)", l) and i + 1 < len(lines) and \
-                lines[i + 1].strip().startswith("s_barrier"):
-            count += 1
-            if last_vmem is None or not PREFETCH.match(last_vmem):
-                bad.append((i, "fall-through", last_vmem))
-            # a loop whose header leads to this barrier: its back edge must end with the prefetch too
-            for j in range(i + 1, len(lines)):
+        m = re.match(r"^\s*s_waitcnt\b.*\bvmcnt\((\d+)\)", l)
+        if not (m and int(m.group(1)) > 0 and i + 1 < len(lines) and lines[i + 1].strip().startswith("s_barrier")):
+            continue
+        n = int(m.group(1))
+        count += 1
+        if not _window_ok(before[i], n):
+            bad.append((i, f"fall-through vmcnt({n})", before[i][-n:]))
+        # a loop header that leads straight to this barrier: every back edge to it must end the same way
+        head = next((k for k in range(i - 1, -1, -1) if LABEL.match(lines[k]) or BRANCH.match(lines[k])), None)
+        if head is not None and LABEL.match(lines[head]) and LABEL.match(lines[head]).group(1) in headers:
+            target = LABEL.match(lines[head]).group(1)
+            for j in range(head + 1, len(lines)):
                 b = BRANCH.match(lines[j])
-                if not b:
-                    continue
-                target = b.group(1) or b.group(2)
-                if target in headers and labels[target] <= i:
-                    prev = last_at[j]
-                    if prev is None or not PREFETCH.match(prev):
-                        bad.append((j, "back edge", prev))
-                    break
+                if b and (b.group(1) or b.group(2)) == target and not _window_ok(before[j], n):
+                    bad.append((j, f"back edge vmcnt({n})", before[j][-n:]))
     return count, bad
 
 
@@ -122,6 +134,16 @@ def test_checker_flags_a_load_moved_past_the_barrier():
     assert run(GOOD) == (1, [])
     back = GOOD.replace("\tbuffer_load_dword v3, v59, s[4:7], s70 offen\n",
                         "\tbuffer_load_dword v3, v59, s[4:7], s70 offen\n\tbuffer_load_dwordx4 v1, s[4:7], s9 offen lds\n")
-    assert [b[1] for b in run(back)[1]] == ["back edge"]
+    assert [b[1] for b in run(back)[1]] == ["back edge vmcnt(1)"]
     entry = GOOD.replace("\tbuffer_load_dword v2, v59, s[4:7], s70 offen\n", "")
-    assert [b[1] for b in run(entry)[1]] == ["fall-through"]
+    assert [b[1] for b in run(entry)[1]] == ["fall-through vmcnt(1)"]
+    # vmcnt(3): the 3 youngest are two copies and the prefetch; a register load among them fails
+    three = GOOD.replace("vmcnt(1)", "vmcnt(3)").replace(
+        "\tbuffer_load_dword v2, v59, s[4:7], s70 offen\n",
+        "\tbuffer_load_dwordx4 v1, s[4:7], s9 offen lds\n\tbuffer_load_dword v2, v59, s[4:7], s70 offen\n").replace(
+        "\tbuffer_load_dword v3, v59, s[4:7], s70 offen\n",
+        "\tbuffer_load_dwordx4 v1, s[4:7], s9 offen lds\n\tbuffer_load_dword v3, v59, s[4:7], s70 offen\n")
+    assert run(three) == (1, [])
+    reg = three.replace("\tbuffer_load_dwordx4 v1, s[4:7], s9 offen lds\n\tbuffer_load_dword v2,",
+                        "\tbuffer_load_dwordx4 v[8:11], v5, s[0:3], s9 offen\n\tbuffer_load_dword v2,")
+    assert [b[1] for b in run(reg)[1]] == ["fall-through vmcnt(3)"]
