@@ -9,10 +9,11 @@ register).  That is exact only while the emitted order is the written one, on
 the fall-through path and on a loop's back edge alike.  The loaded row pointers
 are restrict-qualified, so the compiler is free to move a plain load (a variant
 that staged token rows through registers had its loads sunk past a barrier
-that way).  This test compiles tiled_gemm.hip to assembly and checks, before
-every counted barrier (vmcnt(N) with N > 0, then s_barrier) of every tiled
-kernel: the N youngest vector-memory instructions are LDS copies, except that
-the youngest may be the prefetch, and for vmcnt(1) it must be.
+that way).  These tests compile tiled_gemm.hip and backward.hip to assembly
+and check, before every counted barrier (vmcnt(N) with N > 0, then s_barrier)
+of every tiled and backward GEMM kernel: the N youngest vector-memory
+instructions are LDS copies, except that the youngest may be the prefetch, and
+for vmcnt(1) it must be.
 """
 import os
 import re
@@ -41,23 +42,32 @@ def _instructions(text):
     return out
 
 
-def _kernels(asm):
-    """{symbol: ([instruction lines], {loop header labels})} for each tiled_kernel instantiation."""
+def _kernels(asm, kernel="tiled_kernel"):
+    """{symbol: ([instruction lines], {loop header labels})} for each instantiation of `kernel`."""
     kernels = {}
-    for m in re.finditer(r"^(_ZN\w*tiled_kernel\w*):.*?$(.*?)^\.Lfunc_end\d+:", asm, re.M | re.S):
+    for m in re.finditer(r"^(_ZN\w*" + kernel + r"\w*):.*?$(.*?)^\.Lfunc_end\d+:", asm, re.M | re.S):
         headers = set(re.findall(r"^(\.LBB\w+):\s*;.*Loop Header", m.group(2), re.M))
         kernels[m.group(1)] = (_instructions(m.group(2)), headers)
     return kernels
 
 
-@pytest.fixture(scope="module")
-def tiled_asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "tiled_gemm.s"
-    src = os.path.join(B.CSRC, "tiled_gemm.hip")
+def _asm(tmp_path_factory, name):
+    out = tmp_path_factory.mktemp("asm") / (name + ".s")
+    src = os.path.join(B.CSRC, name + ".hip")
     r = subprocess.run([B.hipcc(), *B.HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", str(out)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def tiled_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "tiled_gemm")
+
+
+@pytest.fixture(scope="module")
+def backward_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "backward")
 
 
 def _window_ok(window, n):
@@ -110,6 +120,16 @@ def test_prefetch_is_the_last_load_before_counted_barriers(tiled_asm):
         assert not bad, (name, bad[:5])
     # the down projection and the prefetching gate/up tiles both have such barriers
     assert total > 0
+
+
+def test_backward_gemm_counted_barriers(backward_asm):
+    """The backward GEMM's ring of four 32-k stages: each stage's barrier leaves
+    the copies of the later stages in flight, and only those."""
+    kernels = _kernels(backward_asm, "bwd_gemm_kernel")
+    assert len(kernels) >= 3, list(kernels)
+    for name, (lines, headers) in kernels.items():
+        count, bad = _check(lines, headers)
+        assert count > 0 and not bad, (name, count, bad[:5])
 
 
 GOOD = """
