@@ -86,7 +86,7 @@ struct LayerWs {
     void* h;
     float* y_perm;
     float* y_perm_hi;  // second K-partial of the tiled down projection, or nullptr
-    float* y_tail_hi;  // second K-partial of the down tail pass [n * 64, d], or nullptr
+    float* y_tail_hi;  // second K-partial of the down tail pass [n * kTailRows, d], or nullptr
     size_t bytes;
 };
 

@@ -132,12 +132,12 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& q, bf16x8_t& lo, b
 // FP8 weights: a stage is 128 k (still 128 bytes per row); step u (64 k)
 // reads chunk 4u + g, i.e. 16 weights k = 64u + 16g .. +16, which feed two
 // MFMAs (k 0-7 and 8-15 of the chunk); the token row is read at the same k.
-template <int NTP, bool COPY, bool FP8>
+template <int NTP, bool COPY, bool FP8, int MT>
 __device__ __forceinline__ void stream_stage(const StreamCtx& c, const uint4* __restrict__ cur,
                                              uint4* __restrict__ nxt, int s,
-                                             const bf16_t* const (&arow)[kStreamMaxTB],
-                                             const uint32_t (&amask)[kStreamMaxTB],
-                                             f32x4_t (&acc)[kStreamMaxTB][kStreamRB]) {
+                                             const bf16_t* const (&arow)[MT],
+                                             const uint32_t (&amask)[MT],
+                                             f32x4_t (&acc)[MT][kStreamRB]) {
     constexpr int kTV = FP8 ? 4 : 2;  // 8-element token fragments per stage
     u32x4_t tv[NTP][kTV];
 #pragma unroll
@@ -184,24 +184,24 @@ __device__ __forceinline__ void stream_stage(const StreamCtx& c, const uint4* __
 }
 
 // The K loop of one pass over NTP token blocks: ns stages (ns even, >= 2).
-template <int NTP, bool FP8>
+template <int NTP, bool FP8, int MT>
 __device__ __forceinline__ void stream_k_loop(const StreamCtx& c, uint4* sb0, uint4* sb1, int ns,
-                                              const bf16_t* const (&arow)[kStreamMaxTB],
-                                              const uint32_t (&amask)[kStreamMaxTB],
-                                              f32x4_t (&acc)[kStreamMaxTB][kStreamRB]) {
+                                              const bf16_t* const (&arow)[MT],
+                                              const uint32_t (&amask)[MT],
+                                              f32x4_t (&acc)[MT][kStreamRB]) {
     stream_copy(c, sb0, 0);
     int s = 0;
     for (; s + 2 < ns; s += 2) {
-        stream_stage<NTP, true, FP8>(c, sb0, sb1, s, arow, amask, acc);
-        stream_stage<NTP, true, FP8>(c, sb1, sb0, s + 1, arow, amask, acc);
+        stream_stage<NTP, true, FP8, MT>(c, sb0, sb1, s, arow, amask, acc);
+        stream_stage<NTP, true, FP8, MT>(c, sb1, sb0, s + 1, arow, amask, acc);
     }
-    stream_stage<NTP, true, FP8>(c, sb0, sb1, s, arow, amask, acc);
-    stream_stage<NTP, false, FP8>(c, sb1, sb0, s + 1, arow, amask, acc);
+    stream_stage<NTP, true, FP8, MT>(c, sb0, sb1, s, arow, amask, acc);
+    stream_stage<NTP, false, FP8, MT>(c, sb1, sb0, s + 1, arow, amask, acc);
 }
 
 // FP8: wa/wb hold E4M3 codes and sa/sb one fp32 scale per weight row, applied
 // to the K sums before the epilogue; otherwise bf16 weights and no scales.
-template <bool DUAL, bool FP8>
+template <bool DUAL, bool FP8, int MT = kStreamMaxTB>
 __global__ __launch_bounds__(256) void stream_kernel(
     const bf16_t* __restrict__ act, const int32_t* __restrict__ row_src,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
@@ -275,17 +275,17 @@ __global__ __launch_bounds__(256) void stream_kernel(
         for (int t = 0; t < 2; ++t) c.rd[t] = c.slice + r * 8 + ((4 * t + g) ^ stream_swz(r));
     }
 
-    for (int tb0 = 0; tb0 < ntb; tb0 += kStreamMaxTB) {
-        const int ntp = min(kStreamMaxTB, ntb - tb0);
+    for (int tb0 = 0; tb0 < ntb; tb0 += MT) {
+        const int ntp = min(MT, ntb - tb0);
         // Activation row of this lane in each token block, at the wave's k
         // origin and this lane's k-group; rows past the segment read the
         // segment's first row and are masked to zero.
-        const bf16_t* arow[kStreamMaxTB];
-        uint32_t amask[kStreamMaxTB];
+        const bf16_t* arow[MT];
+        uint32_t amask[MT];
         const int src0 = DUAL ? row_src[seg] : 0;
         const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? static_cast<int>(static_cast<uint32_t>(src0) / static_cast<uint32_t>(topk)) : 0) : seg;
 #pragma unroll
-        for (int tb = 0; tb < kStreamMaxTB; ++tb) {
+        for (int tb = 0; tb < MT; ++tb) {
             const int p = seg + (tb0 + tb) * 16 + r;
             int row = row0;
             bool real = false;
@@ -303,22 +303,31 @@ __global__ __launch_bounds__(256) void stream_kernel(
             amask[tb] = real ? 0xffffffffu : 0u;
         }
 
-        f32x4_t acc[kStreamMaxTB][kStreamRB];
+        f32x4_t acc[MT][kStreamRB];
 #pragma unroll
-        for (int tb = 0; tb < kStreamMaxTB; ++tb)
+        for (int tb = 0; tb < MT; ++tb)
 #pragma unroll
             for (int b = 0; b < kStreamRB; ++b) acc[tb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         switch (ntp) {
-            case 1: stream_k_loop<1, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
-            case 2: stream_k_loop<2, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
-            case 3: stream_k_loop<3, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
-            default: stream_k_loop<4, FP8>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 1: stream_k_loop<1, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 2: stream_k_loop<2, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 3: stream_k_loop<3, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+            case 4: stream_k_loop<4, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+            default:
+                if constexpr (MT == 8) {
+                    switch (ntp) {
+                        case 5: stream_k_loop<5, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+                        case 6: stream_k_loop<6, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+                        case 7: stream_k_loop<7, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+                        default: stream_k_loop<8, FP8, MT>(c, sb0, sb1, ns, arow, amask, acc); break;
+                    }
+                }
+                break;
         }
 
         // Cross-wave K reduction in a fixed order through the stage buffers,
-        // then wave w finishes token block w.
-        __syncthreads();
+        // four token blocks at a time (wave w finishes token block q + w).
         f32x4_t* red0 = reinterpret_cast<f32x4_t*>(sb0);  // waves 0, 1
         f32x4_t* red1 = reinterpret_cast<f32x4_t*>(sb1);  // waves 2, 3
         auto red = [&](int w, int tb, int b) -> f32x4_t& {
@@ -326,48 +335,53 @@ __global__ __launch_bounds__(256) void stream_kernel(
             return (w < 2 ? red0 : red1)[i];
         };
 #pragma unroll
-        for (int tb = 0; tb < kStreamMaxTB; ++tb)
-            if (tb < ntp)
+        for (int q = 0; q < MT; q += kStreamMaxTB) {
+            if (q >= ntp) continue;  // uniform: ntp is the same for the whole block
+            __syncthreads();
 #pragma unroll
-                for (int b = 0; b < kStreamRB; ++b) red(wave, tb, b) = acc[tb][b];
-        __syncthreads();
-        if (wave < ntp && seg + (tb0 + wave) * 16 + r < seg_end) {
-            const int tb = wave;
-            f32x4_t sum[kStreamRB];
+            for (int tb = 0; tb < kStreamMaxTB; ++tb)
+                if (q + tb < ntp)
 #pragma unroll
-            for (int b = 0; b < kStreamRB; ++b) {
-                sum[b] = red(0, tb, b);
-#pragma unroll
-                for (int w = 1; w < 4; ++w) sum[b] += red(w, tb, b);
-            }
-            // C layout of 16x16 MFMA: lane l holds column (token) l%16 and rows
-            // (weight rows) 4*(l/16) + i, i = 0..3.
-            const int p = seg + (tb0 + tb) * 16 + r;
-            if (DUAL) {
-                const int f0 = blockIdx.x * 32;
-                bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * Nw;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    f32x4_t a1 = sum[half], a3 = sum[half + 2];
-                    if constexpr (FP8) {
-                        const size_t f = static_cast<size_t>(e) * Nw + f0 + half * 16 + 4 * g;
-                        a1 *= *reinterpret_cast<const f32x4_t*>(sa + f);
-                        a3 *= *reinterpret_cast<const f32x4_t*>(sb + f);
-                    }
-                    uint2 o;
-                    o.x = pack_bf16x2(silu_f32(a1[0]) * a3[0], silu_f32(a1[1]) * a3[1]);
-                    o.y = pack_bf16x2(silu_f32(a1[2]) * a3[2], silu_f32(a1[3]) * a3[3]);
-                    *reinterpret_cast<uint2*>(hrow + f0 + half * 16 + 4 * g) = o;
-                }
-            } else {
-                const int j0 = blockIdx.x * 64;
-                float* yrow = part ? out_hi + static_cast<size_t>(e * kTailRows + (p - tail0)) * Nw
-                                   : static_cast<float*>(out) + static_cast<size_t>(p) * Nw;
+                    for (int b = 0; b < kStreamRB; ++b) red(wave, tb, b) = acc[q + tb][b];
+            __syncthreads();
+            if (q + wave < ntp && seg + (tb0 + q + wave) * 16 + r < seg_end) {
+                const int tb = wave;
+                f32x4_t sum[kStreamRB];
 #pragma unroll
                 for (int b = 0; b < kStreamRB; ++b) {
-                    if constexpr (FP8)
-                        sum[b] *= *reinterpret_cast<const f32x4_t*>(sa + static_cast<size_t>(e) * Nw + j0 + b * 16 + 4 * g);
-                    *reinterpret_cast<f32x4_t*>(yrow + j0 + b * 16 + 4 * g) = sum[b];
+                    sum[b] = red(0, tb, b);
+#pragma unroll
+                    for (int w = 1; w < 4; ++w) sum[b] += red(w, tb, b);
+                }
+                // C layout of 16x16 MFMA: lane l holds column (token) l%16 and rows
+                // (weight rows) 4*(l/16) + i, i = 0..3.
+                const int p = seg + (tb0 + q + tb) * 16 + r;
+                if (DUAL) {
+                    const int f0 = blockIdx.x * 32;
+                    bf16_t* hrow = static_cast<bf16_t*>(out) + static_cast<size_t>(p) * Nw;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        f32x4_t a1 = sum[half], a3 = sum[half + 2];
+                        if constexpr (FP8) {
+                            const size_t f = static_cast<size_t>(e) * Nw + f0 + half * 16 + 4 * g;
+                            a1 *= *reinterpret_cast<const f32x4_t*>(sa + f);
+                            a3 *= *reinterpret_cast<const f32x4_t*>(sb + f);
+                        }
+                        uint2 o;
+                        o.x = pack_bf16x2(silu_f32(a1[0]) * a3[0], silu_f32(a1[1]) * a3[1]);
+                        o.y = pack_bf16x2(silu_f32(a1[2]) * a3[2], silu_f32(a1[3]) * a3[3]);
+                        *reinterpret_cast<uint2*>(hrow + f0 + half * 16 + 4 * g) = o;
+                    }
+                } else {
+                    const int j0 = blockIdx.x * 64;
+                    float* yrow = part ? out_hi + static_cast<size_t>(e * kTailRows + (p - tail0)) * Nw
+                                       : static_cast<float*>(out) + static_cast<size_t>(p) * Nw;
+#pragma unroll
+                    for (int b = 0; b < kStreamRB; ++b) {
+                        if constexpr (FP8)
+                            sum[b] *= *reinterpret_cast<const f32x4_t*>(sa + static_cast<size_t>(e) * Nw + j0 + b * 16 + 4 * g);
+                        *reinterpret_cast<f32x4_t*>(yrow + j0 + b * 16 + 4 * g) = sum[b];
+                    }
                 }
             }
         }
@@ -522,16 +536,16 @@ hipError_t launch_down(const Shape& s, int tile_m, const void* h, const int32_t*
         if (ks_max != nullptr) *ks_max = ks;
         hipError_t err = launch_tiled(s, false, h, nullptr, counts, offsets, w2, nullptr, y_perm, st, ks, kTailRows);
         if (err != hipSuccess) return err;
-        // The tails (a few experts' w2, streamed with at most 64 rows each) run
-        // one block per 64 rows of w2 per expert; with a tail buffer they also
+        // The tails (a few experts' w2, streamed with at most kTailRows rows
+        // each, all of them in one pass over the weights) run one block per
+        // 64 rows of w2 per expert; with a tail buffer they also
         // cut K in two, which doubles the blocks of this latency-bound pass
         // (measured at prefill: 140 -> 90-98 us).
         const int parts = (y_tail_hi != nullptr && s.F % 1024 == 0) ? 2 : 1;
         dim3 grid(s.d / 64, s.n, parts);
-        stream_kernel<false, false><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(h), nullptr, counts, offsets,
-                                                          w2, nullptr, nullptr, nullptr, y_perm, s.F, s.d, s.F,
-                                                          s.T * s.K, pmax_rows(s, 256), s.K, kTailRows,
-                                                          parts == 2 ? y_tail_hi : nullptr, ks);
+        stream_kernel<false, false, kTailRows / 16><<<grid, 256, 0, st>>>(
+            static_cast<const bf16_t*>(h), nullptr, counts, offsets, w2, nullptr, nullptr, nullptr, y_perm, s.F, s.d,
+            s.F, s.T * s.K, pmax_rows(s, 256), s.K, kTailRows, parts == 2 ? y_tail_hi : nullptr, ks);
     }
     return hipGetLastError();
 }

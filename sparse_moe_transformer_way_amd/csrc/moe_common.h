@@ -72,7 +72,7 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 // kernels take over from them in the tile-256 layout: such a tail would cost a
 // whole tile there, while streaming reads the expert's weights once.
 constexpr int kTiledRows = 256;
-constexpr int kTailRows = 64;
+constexpr int kTailRows = 128;
 constexpr int kComputeUnits = 256;  // MI355X: a round of tiled-kernel tiles
 
 // Layout of the backward pass's fp32 pre-activations a = [a1 | a3], logically

@@ -62,18 +62,22 @@ def test_layer_small(dtype, T, d, F):
     check_full(inp, TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
+TAIL_ROWS = 128  # the longest tail past an expert's full 256-row tiles that the streaming pass takes
+
+
 def down_plan(counts, d, F, T, K=2, n=8):
     """The down projection's plan that the library takes on the device: the
     largest K split allowed (2 when the worst-case tiles fill fewer than four
     rounds of 256 workgroups), then for each split whether the experts' short
-    tails (at most 64 rows past their full 256-row tiles) go to the streaming
-    pass (when that lowers the number of rounds), and the split whose rounds x
-    K per tile is smallest (no split on a tie).  Returns (K parts, tails streamed)."""
+    tails (at most TAIL_ROWS rows past their full 256-row tiles) go to the
+    streaming pass (when that lowers the number of rounds), and the split whose
+    rounds x K per tile is smallest (no split on a tie).  Returns (K parts,
+    tails streamed)."""
     P = T * K + n * 255
     n_tt, n_wt = -(-P // 256), d // 256
     ks_max = 2 if (n_tt * n_wt < 4 * 256 and (F // 2) % 256 == 0) else 1
     without = sum(-(-c // 256) for c in counts)
-    with_tail = sum(c // 256 if 0 < c % 256 <= 64 else -(-c // 256) for c in counts)
+    with_tail = sum(c // 256 if 0 < c % 256 <= TAIL_ROWS else -(-c // 256) for c in counts)
     best = None
     for ks in range(1, ks_max + 1):
         r_with = -(-with_tail * n_wt * ks // 256)
@@ -85,19 +89,25 @@ def down_plan(counts, d, F, T, K=2, n=8):
     return best[0], best[1]
 
 
-# d = 4096 with a small F at T = 1150: every expert gets 255-316 rows, so the
-# down projection cuts K in two and hands the tails to the streaming pass.
-# With F = 1536 the tail pass runs in one K part (its rows have no second
-# partial); with F = 2048 it cuts K in two into the tail buffer.
-@pytest.mark.parametrize("F,seed", [(1536, 1), (2048, 0)])
-def test_layer_down_tail_pass(F, seed):
-    T, d = 1150, 4096
+# d = 4096 with a small F.  At T = 1150 every expert gets 255-316 rows, so the
+# down projection cuts K in two and hands the tails (under 64 rows) to the
+# streaming pass.  At T = 2300 the experts get 549-615 rows: tails of 37-103
+# rows, several past 64 (the pass then takes 5-8 token blocks of 16 rows in one
+# pass over the weights), and streaming them saves a round with K uncut.  With
+# F = 1536 the tail pass runs in one K part (its rows have no second partial);
+# with F = 2048 it cuts K in two into the tail buffer.
+@pytest.mark.parametrize("T,F,seed,ks_want", [(1150, 1536, 1, 2), (1150, 2048, 0, 2),
+                                              (2300, 2048, 0, 1), (2300, 1536, 2, 1)])
+def test_layer_down_tail_pass(T, F, seed, ks_want):
+    d = 4096
     inp = margin_filtered(mi.make_layer(T, d, F, seed=seed, workload=305))
     counts = np.bincount(oracle.gating(inp.x.float().numpy(), inp.wg.numpy())[1].ravel(), minlength=8)
     ks, tail = down_plan(counts.tolist(), d, F, T)
-    assert ks == 2 and tail, (counts, ks, tail)
+    assert ks == ks_want and tail, (counts, ks, tail)
+    if T == 2300:
+        assert any(64 < c % 256 <= TAIL_ROWS for c in counts), counts
     err = check_full(inp, TOL_BF16)
-    print(f"down tail pass, F={F}: counts {counts.tolist()}, max per-token rel err {err:.3e}")
+    print(f"down tail pass, T={T}, F={F}: counts {counts.tolist()}, max per-token rel err {err:.3e}")
 
 
 def test_tiny_workload():
@@ -186,14 +196,15 @@ def test_workload_full_size(wl, n_rows):
     assert_routing_equal(idx, gate, ref_r, xn, wgn)
     np.testing.assert_array_equal(counts, ref_r["counts"])
     rows = sample_rows(T, ridx, n_rows, seed=wl)
-    # plus tokens whose assignment lands in an expert's short tail (at most 64
-    # rows past its full 256-row tiles): the down projection may compute those
-    # rows in its streaming pass, in two K halves that the combine adds
+    # plus tokens whose assignment lands in an expert's short tail (at most
+    # TAIL_ROWS rows past its full 256-row tiles): the down projection may
+    # compute those rows in its streaming pass, in two K halves that the
+    # combine adds
     grp = oracle.group_by_expert(ridx, 8, 256)
     tails = []
     for e in range(8):
         c, off = int(grp["counts"][e]), int(grp["offsets"][e])
-        if 0 < c % 256 <= 64:
+        if 0 < c % 256 <= TAIL_ROWS:
             tails += (grp["row_src"][off + c - c % 256: off + c] // 2).tolist()
     tail_tokens = np.unique(np.array(tails, np.int64))
     tail_tokens = np.random.default_rng(wl).permutation(tail_tokens)[:48]
