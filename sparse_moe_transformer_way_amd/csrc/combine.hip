@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const float4* p[K];
     const float4* q[K];
     Segments sg;
-    DownPlan plan{1, false};
+    DownPlan plan{1, 0};
     if (HI) {
         load_segments(hp.offsets, hp.counts, hp.n_exp, sg);
         plan = down_plan(sg, hp.n_exp, d / kTiledRows, hp.ks_max);
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         p[s] = reinterpret_cast<const float4*>(y_perm + row);
         q[s] = p[s];
         hkeep[s] = 0u;
-        if (HI && (plan.tail || plan.ks == 2)) {
+        if (HI && (plan.tail_rows > 0 || plan.ks == 2)) {
             // the expert of row rr, its segment start and count, by selects
             // (indexing the register arrays with a run-time index would put
             // them in scratch memory)
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             }
             const int rem = c % kTiledRows;
             const int tail0 = off + c - rem;
-            if (plan.tail && rem > 0 && rem <= kTailRows && rr >= tail0) {
+            if (rem > 0 && rem <= plan.tail_rows && rr >= tail0) {
                 if (hp.y_tail_hi != nullptr) {
                     q[s] = reinterpret_cast<const float4*>(hp.y_tail_hi +
                                                            static_cast<size_t>(e * kTailRows + rr - tail0) * d);

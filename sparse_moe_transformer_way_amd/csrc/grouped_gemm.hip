@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
         if (r == 0 || r > tail_rows) return;
         Segments sg;
         load_segments(offsets, counts, gridDim.y, sg);
-        if (!down_plan(sg, gridDim.y, Nw / kTiledRows, plan_ks_max).tail) return;
+        if (r > down_plan(sg, gridDim.y, Nw / kTiledRows, plan_ks_max).tail_rows) return;
         seg += cnt - r;
         cnt = r;
         tail0 = seg;

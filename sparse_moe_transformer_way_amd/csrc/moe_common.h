@@ -154,15 +154,22 @@ __device__ __forceinline__ void load_segments(const int32_t* offsets, const int3
 //        lowers the K-weighted round count, ceil(2 t / CUs) / 2 < ceil(t / CUs)
 //        for t tiles (a last round of few tiles is then half as long); each
 //        part writes its own fp32 partial sum, which the combine adds.
-//   tail the experts' short tails (at most kTailRows rows past their full
-//        tiles) go to the streaming pass, when that lowers the round count.
+//   tail_rows  the experts' short tails (at most tail_rows rows past their
+//        full tiles) go to the streaming pass, when that lowers the round
+//        count: tails up to kTailRows rows while at most five 4096-wide
+//        experts' worth of tails go there (the pass then stays within about a
+//        round and a quarter of streaming blocks, two per CU with K cut in
+//        two), else tails up to kTailRows / 2 rows.  Measured: with 128-row
+//        tails the 32-block stack ran 3.5% faster; with six streamed tails
+//        (skewed routing) the longer pass cost more than the narrow tiles it
+//        replaced, which is what the cap keeps out.
 struct DownPlan {
     int ks;
-    bool tail;
+    int tail_rows;  // tails of at most this many rows go to the streaming pass (0: none)
 };
 
 __device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int n_wt, int ks_max) {
-    int with_tail = 0, without = 0;
+    int with_short = 0, with_long = 0, without = 0, n_long = 0;
 #pragma unroll
     for (int e = 0; e < kMaxExperts; ++e) {
         if (e < n_exp) {
@@ -170,10 +177,17 @@ __device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int 
             const int c = s.cnt[e];
             const int r = c % kTiledRows;
             without += len / kTiledRows;
-            with_tail += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
+            with_short += (r > 0 && r <= kTailRows / 2) ? c / kTiledRows : len / kTiledRows;
+            with_long += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
+            n_long += (r > 0 && r <= kTailRows) ? 1 : 0;
         }
     }
-    DownPlan best{1, false};
+    // the tail pass runs 8 blocks per tail expert per 256 weight rows (64 rows
+    // each, K in two parts), two per CU: at most 5/4 of a round of them
+    const bool long_ok = 4 * (n_long * n_wt * 8) <= 5 * (2 * kComputeUnits);
+    const int with_tail = long_ok ? with_long : with_short;
+    const int tail_max = long_ok ? kTailRows : kTailRows / 2;
+    DownPlan best{1, 0};
     int best_r = 0;
     for (int ks = 1; ks <= ks_max; ++ks) {
         const int per = n_wt * ks;
@@ -183,7 +197,7 @@ __device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int 
         const int r = tail ? r_with : r_without;
         // r rounds of K / ks each: compare r / ks across ks (the smaller ks on a tie)
         if (ks == 1 || r * best.ks < best_r * ks) {
-            best = DownPlan{ks, tail};
+            best = DownPlan{ks, tail ? tail_max : 0};
             best_r = r;
         }
     }

@@ -797,13 +797,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // compiler's register allocation of the gate/up kernels has no spills
         // (with a plain tail_rows = 0 it spilled SGPRs, and VGPRs to scratch in
         // the pre-activation variant).
-        if (tail_rows > 0 && !down_plan(sg, n_exp, n_wt, ksplit).tail) tail_rows = 0;
+        if (tail_rows > 0) tail_rows = min(tail_rows, down_plan(sg, n_exp, n_wt, ksplit).tail_rows);
     } else {
         // down projection: ksplit is the largest K split allowed, the plan picks
         // the split and whether the short tails go to the streaming pass
         const DownPlan plan = down_plan(sg, n_exp, n_wt, ksplit);
         ksplit = plan.ks;
-        if (!plan.tail) tail_rows = 0;
+        tail_rows = min(tail_rows, plan.tail_rows);
     }
     TileId t;
     if (!(DUAL ? tile_by_column(sg, n_exp, n_wt, ksplit, tail_rows, t)
