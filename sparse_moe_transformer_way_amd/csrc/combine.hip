@@ -123,11 +123,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     uint32_t hkeep[K];  // all ones where the slot's row has a second K-partial
     const float4* p[K];
     const float4* q[K];
-    Segments sg;
+    LaneSeg ls{0, 0, 0};
     DownPlan plan{1, 0};
     if (HI) {
-        load_segments(hp.offsets, hp.counts, hp.n_exp, sg);
-        plan = down_plan(sg, hp.n_exp, d / kTiledRows, hp.ks_max);
+        ls = lane_segment(hp.offsets, hp.counts, hp.n_exp);
+        plan = down_plan(ls, d / kTiledRows, hp.ks_max);
     }
 #pragma unroll
     for (int s = 0; s < K; ++s) {
@@ -140,17 +140,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         q[s] = p[s];
         hkeep[s] = 0u;
         if (HI && (plan.tail_rows > 0 || plan.ks == 2)) {
-            // the expert of row rr, its segment start and count, by selects
-            // (indexing the register arrays with a run-time index would put
-            // them in scratch memory)
-            int e = 0, off = sg.off[0], c = sg.cnt[0];
-#pragma unroll
-            for (int j = 1; j < kMaxExperts; ++j) {
-                const bool in = j < hp.n_exp && rr >= sg.off[j];
-                e = in ? j : e;
-                off = in ? sg.off[j] : off;
-                c = in ? sg.cnt[j] : c;
-            }
+            // the expert of row rr (the same in every lane: one token per
+            // block): the last expert whose segment starts at or before it
+            const int ru = __builtin_amdgcn_readfirstlane(rr);
+            const uint64_t at = __ballot(static_cast<int>(threadIdx.x & 63) < hp.n_exp && ls.off <= ru);
+            const int e = at == 0 ? 0 : 63 - static_cast<int>(__builtin_clzll(at));
+            const int off = __builtin_amdgcn_readlane(ls.off, e);
+            const int c = __builtin_amdgcn_readlane(ls.cnt, e);
             const int rem = c % kTiledRows;
             const int tail0 = off + c - rem;
             if (rem > 0 && rem <= plan.tail_rows && rr >= tail0) {

@@ -232,9 +232,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
         // Nw / 64 here; the tiled kernel's weight tiles are Nw / 256).
         const int r = cnt % kTiledRows;
         if (r == 0 || r > tail_rows) return;
-        Segments sg;
-        load_segments(offsets, counts, gridDim.y, sg);
-        if (r > down_plan(sg, gridDim.y, Nw / kTiledRows, plan_ks_max).tail_rows) return;
+        const LaneSeg ls = lane_segment(offsets, counts, gridDim.y);
+        if (r > down_plan(ls, Nw / kTiledRows, plan_ks_max).tail_rows) return;
         seg += cnt - r;
         cnt = r;
         tail0 = seg;

@@ -131,20 +131,55 @@ __device__ __forceinline__ void store_rows_staged(const f32x16_t (&acc)[4][4], f
 constexpr int kMaxExperts = 16;
 constexpr int kMaxTopK = 4;
 
-// Every expert's segment offset and count.  All loads are issued before any is
-// used (indices clamped into the arrays), so a kernel's prologue waits one
-// memory latency for them, not one per expert as a loop that loads as it goes.
-struct Segments {
-    int off[kMaxExperts + 1];
-    int cnt[kMaxExperts];
+// Every expert's segment, one expert per lane: in each group of 16 lanes,
+// lane e < n_exp holds expert e's offset, end and count, the other lanes an
+// empty segment.  Kernels that
+// need a sum or a search over the experts do it across the lanes (a few
+// shuffles and a ballot) rather than as a loop over 16 expert slots in scalar
+// registers: such a loop is a chain of several hundred dependent scalar
+// instructions, which a wave issues one per 4 cycles (~1-2 us at the clock the
+// chip holds under load, paid by every workgroup).  Every lane of the wave
+// must be active where these are called.
+struct LaneSeg {
+    int off, end, cnt;
 };
 
-__device__ __forceinline__ void load_segments(const int32_t* offsets, const int32_t* counts, int n_exp,
-                                              Segments& s) {
+__device__ __forceinline__ LaneSeg lane_segment(const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ counts, int n_exp) {
+    const int e = threadIdx.x & 15;
+    LaneSeg s{0, 0, 0};
+    if (e < n_exp) {
+        s.off = offsets[e];
+        s.end = offsets[e + 1];
+        s.cnt = counts[e];
+    }
+    return s;
+}
+
+// Sum of v over lanes 0-15 (the expert lanes), the same in every lane.
+__device__ __forceinline__ int expert_sum(int v) {
 #pragma unroll
-    for (int j = 0; j <= kMaxExperts; ++j) s.off[j] = offsets[min(j, n_exp)];
+    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Inclusive prefix sum of v over lanes 0-15 (lanes past 15 keep their sums
+// of their own group of 16, which no caller reads).
+__device__ __forceinline__ int expert_prefix(int v) {
+    const int lane = threadIdx.x & 15;
 #pragma unroll
-    for (int j = 0; j < kMaxExperts; ++j) s.cnt[j] = counts[min(j, n_exp - 1)];
+    for (int o = 1; o < 16; o <<= 1) {
+        const int u = __shfl_up(v, o, 16);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// The lane of the first expert whose inclusive prefix ps exceeds i (uniform
+// i, 0 <= i < the total), or -1.
+__device__ __forceinline__ int expert_holding(int ps, int i) {
+    const uint64_t hit = __ballot((threadIdx.x & 63) < 16 && ps > i);
+    return hit == 0 ? -1 : static_cast<int>(__builtin_ctzll(hit));
 }
 
 // The down projection's plan for one call, taken on the device from the real
@@ -168,20 +203,16 @@ struct DownPlan {
     int tail_rows;  // tails of at most this many rows go to the streaming pass (0: none)
 };
 
-__device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int n_wt, int ks_max) {
-    int with_short = 0, with_long = 0, without = 0, n_long = 0;
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) {
-        if (e < n_exp) {
-            const int len = s.off[e + 1] - s.off[e];
-            const int c = s.cnt[e];
-            const int r = c % kTiledRows;
-            without += len / kTiledRows;
-            with_short += (r > 0 && r <= kTailRows / 2) ? c / kTiledRows : len / kTiledRows;
-            with_long += (r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows;
-            n_long += (r > 0 && r <= kTailRows) ? 1 : 0;
-        }
-    }
+__device__ __forceinline__ DownPlan down_plan(const LaneSeg& s, int n_wt, int ks_max) {
+    // per expert (lane), then summed over the experts
+    const int len = s.end - s.off;
+    const int c = s.cnt;
+    const int r = c % kTiledRows;
+    const int without = expert_sum(len / kTiledRows);
+    const int with_short = expert_sum((r > 0 && r <= kTailRows / 2) ? c / kTiledRows : len / kTiledRows);
+    const int with_long = expert_sum((r > 0 && r <= kTailRows) ? c / kTiledRows : len / kTiledRows);
+    const int n_long = expert_sum((r > 0 && r <= kTailRows) ? 1 : 0);
+    // (lanes past the experts hold empty segments, which add nothing)
     // the tail pass runs 8 blocks per tail expert per 256 weight rows (64 rows
     // each, K in two parts), two per CU: at most 5/4 of a round of them
     const bool long_ok = 4 * (n_long * n_wt * 8) <= 5 * (2 * kComputeUnits);
@@ -194,11 +225,11 @@ __device__ __forceinline__ DownPlan down_plan(const Segments& s, int n_exp, int 
         const int r_with = (with_tail * per + kComputeUnits - 1) / kComputeUnits;
         const int r_without = (without * per + kComputeUnits - 1) / kComputeUnits;
         const bool tail = r_with < r_without;
-        const int r = tail ? r_with : r_without;
-        // r rounds of K / ks each: compare r / ks across ks (the smaller ks on a tie)
-        if (ks == 1 || r * best.ks < best_r * ks) {
+        const int rr = tail ? r_with : r_without;
+        // rr rounds of K / ks each: compare rr / ks across ks (the smaller ks on a tie)
+        if (ks == 1 || rr * best.ks < best_r * ks) {
             best = DownPlan{ks, tail ? tail_max : 0};
-            best_r = r;
+            best_r = rr;
         }
     }
     return best;

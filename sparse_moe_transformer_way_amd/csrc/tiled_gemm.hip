@@ -92,6 +92,12 @@ __device__ __forceinline__ int token_tiles(int len, int count, int tail_rows) {
     return (r > 0 && r <= tail_rows) ? count / kTT : len / kTT;
 }
 
+// a / topk for topk in 1..4 (uniform): shifts, and for 3 a multiply-high by
+// ceil(2^33 / 3), exact for every 32-bit a
+__device__ __forceinline__ uint32_t div_topk(uint32_t a, int topk) {
+    return topk == 2 ? a >> 1 : topk == 4 ? a >> 2 : topk == 3 ? __umulhi(a, 0xAAAAAAABu) >> 1 : a;
+}
+
 // Buffer resource over [base, base + 4 GiB); every offset the kernel adds is
 // in range by construction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -558,7 +564,7 @@ __device__ __forceinline__ void narrow_tile(const TileCtx& c, const bf16_t* __re
                 if (src < 0 || src >= n_src) src = 0;
                 const int ch = (((r0 + 8 * jj) >> 4) & 1) ? ch1 : ch0;
                 n.to[jj] = static_cast<uint32_t>(
-                    (static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act + 8 * ch) * 2);
+                    (static_cast<size_t>(div_topk(static_cast<uint32_t>(src), topk)) * ld_act + 8 * ch) * 2);
             }
             n.tstride = 0;
         } else {
@@ -679,16 +685,13 @@ struct TileId {
 
 // Down projection: XCD x takes the x-th of 8 equal contiguous runs of the
 // expert-major enumeration (K part, expert, group).  The token side (h rows,
-// 28 KB each) is then read by one or two XCDs only.
-__device__ __forceinline__ bool tile_contiguous(const Segments& sg, int n_exp, int n_wt, int ksplit, int tail_rows,
-                                                TileId& t) {
-    int ntt[kMaxExperts];
-    int per_split = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxExperts; ++j) {
-        ntt[j] = j < n_exp ? token_tiles(sg.off[j + 1] - sg.off[j], sg.cnt[j], tail_rows) : 0;
-        per_split += ntt[j] * n_wt;
-    }
+// 28 KB each) is then read by one or two XCDs only.  The expert is found
+// across the expert lanes (prefix sum and ballot).
+__device__ __forceinline__ bool tile_contiguous(const LaneSeg& s, int n_wt, int ksplit, int tail_rows, TileId& t) {
+    const int ntt = token_tiles(s.end - s.off, s.cnt, tail_rows);  // 0 for an empty segment
+    const int w = ntt * n_wt;
+    const int ps = expert_prefix(w);
+    const int per_split = __builtin_amdgcn_readlane(ps, 15);
     const int total = per_split * ksplit;
     const int run = (total + 7) >> 3;
     if (static_cast<int>(blockIdx.x >> 3) >= run) return false;
@@ -696,24 +699,14 @@ __device__ __forceinline__ bool tile_contiguous(const Segments& sg, int n_exp, i
     if (L_all >= total) return false;
     t.split = L_all / per_split;
     int L = L_all - t.split * per_split;
-    int nt = 0;
-    bool hit = false;
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) {
-        if (!hit && e < n_exp) {
-            if (L < ntt[e] * n_wt) {
-                hit = true;
-                t.e = e;
-                nt = ntt[e];
-                t.seg = sg.off[e];
-                t.seg_end = sg.off[e + 1];
-                t.cnt = sg.cnt[e];
-            } else {
-                L -= ntt[e] * n_wt;
-            }
-        }
-    }
-    if (!hit) return false;
+    const int h = expert_holding(ps, L);
+    if (h < 0) return false;
+    L -= __builtin_amdgcn_readlane(ps - w, h);
+    t.e = h;
+    t.seg = __builtin_amdgcn_readlane(s.off, h);
+    t.seg_end = __builtin_amdgcn_readlane(s.end, h);
+    t.cnt = __builtin_amdgcn_readlane(s.cnt, h);
+    const int nt = __builtin_amdgcn_readlane(ntt, h);
     const int gn = max(1, min(n_wt, kXcdTiles / nt));
     const int g = L / (gn * nt);
     const int rem = L - g * gn * nt;
@@ -732,41 +725,45 @@ __device__ __forceinline__ bool tile_contiguous(const Segments& sg, int n_exp, i
 // tiles stay on one XCD, so the weights keep their L2 reuse; the gathered
 // token rows (x is 32 MB) are read by every XCD.  An XCD holds at most
 // ceil(n_wt / 8) columns of an expert: its count exceeds total / 8 by at most
-// the number of token tiles, which the grid allows for.  ksplit <= 2.
-__device__ __forceinline__ bool tile_by_column(const Segments& sg, int n_exp, int n_wt, int ksplit, int tail_rows,
-                                               TileId& t) {
+// the number of token tiles, which the grid allows for.  ksplit <= 2.  Lane
+// j < 32 stands for (K part j / 16, expert j % 16) and holds that pair's tile
+// count on this XCD; a prefix sum over those lanes and a ballot find the pair
+// that holds the workgroup's tile.  Gate/up keeps every token tile (its short
+// tails run as narrow tiles).
+__device__ __forceinline__ bool tile_by_column(const LaneSeg& s, int n_exp, int n_wt, int ksplit, TileId& t) {
+    const int lane = threadIdx.x & 63;
     const int x = blockIdx.x & 7;
-    int i = blockIdx.x >> 3;
-    int nt = 0, first = 0, k = 0;
-    bool hit = false;
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-#pragma unroll
-        for (int e = 0; e < kMaxExperts; ++e) {
-            if (!hit && sp < ksplit && e < n_exp) {
-                const int ntt = token_tiles(sg.off[e + 1] - sg.off[e], sg.cnt[e], tail_rows);
-                const int f = (x - ((sp * n_exp + e) * n_wt) % 8 + 8) % 8;  // this XCD's first weight tile
-                const int kk = f < n_wt ? (n_wt - 1 - f) / 8 + 1 : 0;      // its weight tiles of expert e
-                if (i < kk * ntt) {
-                    hit = true;
-                    t.split = sp;
-                    t.e = e;
-                    t.seg = sg.off[e];
-                    t.seg_end = sg.off[e + 1];
-                    t.cnt = sg.cnt[e];
-                    nt = ntt;
-                    first = f;
-                    k = kk;
-                } else {
-                    i -= kk * ntt;
-                }
-            }
-        }
+    const int i = blockIdx.x >> 3;
+    const int sp = lane >> 4;
+    const int e = lane & 15;
+    int ntt = 0, f = 0, kk = 0;
+    if (sp < ksplit && e < n_exp) {
+        ntt = (s.end - s.off) / kTT;
+        f = (x - (((sp * n_exp + e) * n_wt) & 7) + 8) & 7;  // this XCD's first weight tile
+        kk = f < n_wt ? ((n_wt - 1 - f) >> 3) + 1 : 0;     // its weight tiles of expert e
     }
-    if (!hit) return false;
+    const int w = kk * ntt;
+    int ps = w;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        const int u = __shfl_up(ps, o, 64);
+        if (lane >= o) ps += u;
+    }
+    const uint64_t hit = __ballot(lane < 32 && ps > i);
+    if (hit == 0) return false;
+    const int h = static_cast<int>(__builtin_ctzll(hit));
+    const int li = i - __builtin_amdgcn_readlane(ps - w, h);
+    t.split = h >> 4;
+    t.e = h & 15;
+    t.seg = __builtin_amdgcn_readlane(s.off, h);
+    t.seg_end = __builtin_amdgcn_readlane(s.end, h);
+    t.cnt = __builtin_amdgcn_readlane(s.cnt, h);
+    const int nt = __builtin_amdgcn_readlane(ntt, h);
+    const int first = __builtin_amdgcn_readlane(f, h);
+    const int k = __builtin_amdgcn_readlane(kk, h);
     const int gn = max(1, min(k, kXcdTiles / nt));
-    const int g = i / (gn * nt);
-    const int rem = i - g * gn * nt;
+    const int g = li / (gn * nt);
+    const int rem = li - g * gn * nt;
     const int gw = min(gn, k - g * gn);
     t.ttl = rem / gw;
     t.wt = first + 8 * (g * gn + (rem - t.ttl * gw));
@@ -789,26 +786,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- tile of this workgroup (the grid covers the worst case; spare
     // workgroups exit here)
-    Segments sg;
-    load_segments(offsets, counts, n_exp, sg);
-    if (DUAL) {
-        // Gate/up keeps its short tails (as narrow tiles) and its launches pass
-        // no tail_rows, so this test never fires; written this way the
-        // compiler's register allocation of the gate/up kernels has no spills
-        // (with a plain tail_rows = 0 it spilled SGPRs, and VGPRs to scratch in
-        // the pre-activation variant).
-        if (tail_rows > 0) tail_rows = min(tail_rows, down_plan(sg, n_exp, n_wt, ksplit).tail_rows);
-    } else {
-        // down projection: ksplit is the largest K split allowed, the plan picks
-        // the split and whether the short tails go to the streaming pass
-        const DownPlan plan = down_plan(sg, n_exp, n_wt, ksplit);
-        ksplit = plan.ks;
-        tail_rows = min(tail_rows, plan.tail_rows);
-    }
     TileId t;
-    if (!(DUAL ? tile_by_column(sg, n_exp, n_wt, ksplit, tail_rows, t)
-               : tile_contiguous(sg, n_exp, n_wt, ksplit, tail_rows, t)))
-        return;
+    {
+        const LaneSeg ls = lane_segment(offsets, counts, n_exp);
+        if constexpr (DUAL) {
+            // gate/up launches pass no tail_rows
+            if (!tile_by_column(ls, n_exp, n_wt, ksplit, t)) return;
+        } else {
+            // down projection: ksplit is the largest K split allowed, the plan
+            // picks the split and whether the short tails go to the streaming pass
+            const DownPlan plan = down_plan(ls, n_wt, ksplit);
+            ksplit = plan.ks;
+            tail_rows = min(tail_rows, plan.tail_rows);
+            if (!tile_contiguous(ls, n_wt, ksplit, tail_rows, t)) return;
+        }
+    }
     const int split = t.split, e = t.e, ttl = t.ttl, wt = t.wt;
     const int kpart = Kdim / ksplit;
     const int kbase = split * kpart;
@@ -885,7 +877,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 int src = srcs[j];
                 if (src < 0 || src >= n_src) src = 0;
                 c.to[j] = static_cast<uint32_t>(
-                    (static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
+                    (static_cast<size_t>(div_topk(static_cast<uint32_t>(src), topk)) * ld_act + 8 * (((j >> 1) & 1) ? ch1 : ch0)) * 2);
             }
             c.tstride = 0;
         } else {
