@@ -308,12 +308,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wu = wave & 1, wv = wave >> 1;
     const int nut = g.U / kTU;
 
-    // ---- tile of this block: (expert e, u tile ut, v tile vt), XCD-aware
+    // ---- tile of this block: (expert e, u tile ut, v tile vt), XCD-aware.
+    // The search over the experts runs across lanes: lane e (of each 16) holds
+    // expert e's segment, and a prefix sum over those lanes and a ballot find
+    // the expert (a loop over the experts waited one memory latency per expert).
+    const int lane16 = threadIdx.x & 15;
+    const int s0 = lane16 < g.n_exp ? g.offsets[lane16] : 0;
+    const int s1 = lane16 < g.n_exp ? g.offsets[lane16 + 1] : 0;
     int e = 0, ut = 0, vt = 0, kbeg = 0, klen = g.K, ksp = 0;
     if (TOKEN_V) {
         // v runs over the expert's rows: expert e owns nut * (len_e / kTV) tiles
-        int total = 0;
-        for (int j = 0; j < g.n_exp; ++j) total += (g.offsets[j + 1] - g.offsets[j]) / kTV * nut;
+        const int nv = (s1 - s0) / kTV;
+        const int w = nv * nut;
+        const int ps = expert_prefix(w);
+        const int total = __builtin_amdgcn_readlane(ps, 15);
         const int tiles = total * g.ksplit;
         const int run = (tiles + 7) >> 3;
         if (static_cast<int>(blockIdx.x >> 3) >= run) return;
@@ -321,16 +329,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (L >= tiles) return;
         ksp = L / total;
         L -= ksp * total;
-        for (e = 0; e < g.n_exp; ++e) {
-            const int nv = (g.offsets[e + 1] - g.offsets[e]) / kTV;
-            if (L < nv * nut) {
-                ut = L / nv;
-                vt = L - ut * nv;
-                break;
-            }
-            L -= nv * nut;
-        }
-        vt = g.offsets[e] / kTV + vt;  // global v tile (row block of the permuted layout)
+        e = expert_holding(ps, L);
+        if (e < 0) return;
+        L -= __builtin_amdgcn_readlane(ps - w, e);
+        const int nve = __builtin_amdgcn_readlane(nv, e);
+        ut = L / nve;
+        vt = L - ut * nve;
+        vt = __builtin_amdgcn_readlane(s0, e) / kTV + vt;  // global v tile (row block of the permuted layout)
     } else {
         // fixed U x V per expert, K = the expert's rows, which differ between
         // experts (rows padded to 256): the v columns of every expert are dealt
@@ -340,23 +345,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // expert: at prefill four XCDs ran K = 1280 while four ran 1024.)
         const int nvt = g.V / kTV;
         const int x = blockIdx.x & 7;
-        int i = blockIdx.x >> 3;
-        bool hit = false;
-        for (e = 0; e < g.n_exp; ++e) {
-            const int f = (x - (e * nvt) % 8 + 8) % 8;       // this XCD's first column of expert e
-            const int kk = f < nvt ? (nvt - 1 - f) / 8 + 1 : 0;  // its columns of expert e
-            if (i < kk * nut) {
-                const int col = i / nut;
-                ut = i - col * nut;
-                vt = f + 8 * col;
-                hit = true;
-                break;
-            }
-            i -= kk * nut;
+        const int i = blockIdx.x >> 3;
+        int f = 0, kk = 0;
+        if (lane16 < g.n_exp) {
+            f = (x - (lane16 * nvt) % 8 + 8) % 8;       // this XCD's first column of expert lane16
+            kk = f < nvt ? (nvt - 1 - f) / 8 + 1 : 0;  // its columns of that expert
         }
-        if (!hit) return;
-        kbeg = g.offsets[e];
-        klen = g.offsets[e + 1] - kbeg;
+        const int w = kk * nut;
+        const int ps = expert_prefix(w);
+        e = expert_holding(ps, i);
+        if (e < 0) return;
+        const int li = i - __builtin_amdgcn_readlane(ps - w, e);
+        const int col = li / nut;
+        ut = li - col * nut;
+        vt = __builtin_amdgcn_readlane(f, e) + 8 * col;
+        kbeg = __builtin_amdgcn_readlane(s0, e);
+        klen = __builtin_amdgcn_readlane(s1, e) - kbeg;
     }
     const int u0 = ut * kTU, v0 = vt * kTV;
     if (TOKEN_V && g.ksplit > 1) klen = g.K / g.ksplit;
