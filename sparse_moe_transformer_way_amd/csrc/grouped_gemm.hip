@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
         const bf16_t* arow[MT];
         uint32_t amask[MT];
         const int src0 = DUAL ? row_src[seg] : 0;
-        const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? static_cast<int>(static_cast<uint32_t>(src0) / static_cast<uint32_t>(topk)) : 0) : seg;
+        const int row0 = DUAL ? ((src0 >= 0 && src0 < n_src) ? static_cast<int>(div_topk(static_cast<uint32_t>(src0), topk)) : 0) : seg;
 #pragma unroll
         for (int tb = 0; tb < MT; ++tb) {
             const int p = seg + (tb0 + tb) * 16 + r;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 if (DUAL) {
                     const int src = row_src[p];
                     real = src >= 0 && src < n_src;
-                    if (real) row = static_cast<int>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk));
+                    if (real) row = static_cast<int>(div_topk(static_cast<uint32_t>(src), topk));
                 } else {
                     real = true;
                     row = p;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void f32_kernel(
         if (rr < valid) {
             if (DUAL) {
                 const int src = row_src[p0 + rr];
-                if (src >= 0 && src < n_src) arow = act + static_cast<size_t>(static_cast<uint32_t>(src) / static_cast<uint32_t>(topk)) * ld_act;
+                if (src >= 0 && src < n_src) arow = act + static_cast<size_t>(div_topk(static_cast<uint32_t>(src), topk)) * ld_act;
             } else {
                 arow = act + static_cast<size_t>(p0 + rr) * ld_act;
             }

@@ -127,6 +127,13 @@ __device__ __forceinline__ void store_rows_staged(const f32x16_t (&acc)[4][4], f
     }
 }
 
+// a / topk for topk in 1..4 (uniform), the token of an assignment index:
+// shifts, and for 3 a multiply-high by ceil(2^33 / 3), exact for every 32-bit
+// a (a run-time integer division is a few dozen instructions per lane)
+__device__ __forceinline__ uint32_t div_topk(uint32_t a, int topk) {
+    return topk == 2 ? a >> 1 : topk == 4 ? a >> 2 : topk == 3 ? __umulhi(a, 0xAAAAAAABu) >> 1 : a;
+}
+
 // Largest expert count and top-k the kernels are built for (Mixtral: 8, 2).
 constexpr int kMaxExperts = 16;
 constexpr int kMaxTopK = 4;

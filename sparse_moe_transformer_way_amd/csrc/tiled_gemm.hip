@@ -92,12 +92,6 @@ __device__ __forceinline__ int token_tiles(int len, int count, int tail_rows) {
     return (r > 0 && r <= tail_rows) ? count / kTT : len / kTT;
 }
 
-// a / topk for topk in 1..4 (uniform): shifts, and for 3 a multiply-high by
-// ceil(2^33 / 3), exact for every 32-bit a
-__device__ __forceinline__ uint32_t div_topk(uint32_t a, int topk) {
-    return topk == 2 ? a >> 1 : topk == 4 ? a >> 2 : topk == 3 ? __umulhi(a, 0xAAAAAAABu) >> 1 : a;
-}
-
 // Buffer resource over [base, base + 4 GiB); every offset the kernel adds is
 // in range by construction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
