@@ -140,13 +140,12 @@ constexpr int kMaxTopK = 4;
 
 // Every expert's segment, one expert per lane: in each group of 16 lanes,
 // lane e < n_exp holds expert e's offset, end and count, the other lanes an
-// empty segment.  Kernels that
-// need a sum or a search over the experts do it across the lanes (a few
-// shuffles and a ballot) rather than as a loop over 16 expert slots in scalar
-// registers: such a loop is a chain of several hundred dependent scalar
-// instructions, which a wave issues one per 4 cycles (~1-2 us at the clock the
-// chip holds under load, paid by every workgroup).  Every lane of the wave
-// must be active where these are called.
+// empty segment.  Kernels that need a sum or a search over the experts do it
+// across the lanes (a few shuffles and a ballot) rather than as a loop over 16
+// expert slots in scalar registers: such a loop is a chain of several hundred
+// dependent scalar instructions, which a wave issues one per 4 cycles (~1-2 us
+// at the clock the chip holds under load, paid by every workgroup).  Every
+// lane of the wave must be active where these are called.
 struct LaneSeg {
     int off, end, cnt;
 };
@@ -199,9 +198,8 @@ __device__ __forceinline__ int expert_holding(int ps, int i) {
 //   tail_rows  the experts' short tails (at most tail_rows rows past their
 //        full tiles) go to the streaming pass, when that lowers the round
 //        count: tails up to kTailRows rows while at most five 4096-wide
-//        experts' worth of tails go there (the pass then stays within about a
-//        round and a quarter of streaming blocks, two per CU with K cut in
-//        two), else tails up to kTailRows / 2 rows.  Measured: with 128-row
+//        experts' worth of tails go there (at most 640 streaming blocks, K cut
+//        in two), else tails up to kTailRows / 2 rows.  Measured: with 128-row
 //        tails the 32-block stack ran 3.5% faster; with six streamed tails
 //        (skewed routing) the longer pass cost more than the narrow tiles it
 //        replaced, which is what the cap keeps out.
@@ -221,7 +219,7 @@ __device__ __forceinline__ DownPlan down_plan(const LaneSeg& s, int n_wt, int ks
     const int n_long = expert_sum((r > 0 && r <= kTailRows) ? 1 : 0);
     // (lanes past the experts hold empty segments, which add nothing)
     // the tail pass runs 8 blocks per tail expert per 256 weight rows (64 rows
-    // each, K in two parts), two per CU: at most 5/4 of a round of them
+    // each, K in two parts): at most 640 of them
     const bool long_ok = 4 * (n_long * n_wt * 8) <= 5 * (2 * kComputeUnits);
     const int with_tail = long_ok ? with_long : with_short;
     const int tail_max = long_ok ? kTailRows : kTailRows / 2;
