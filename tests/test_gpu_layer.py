@@ -24,7 +24,7 @@ def _gpu():
 
 
 def run_layer(inp, residual=None):
-    desc = moe.make_desc(inp.d, inp.F, dtype=DT[inp.dtype])
+    desc = moe.make_desc(inp.d, inp.F, inp.n, inp.K, dtype=DT[inp.dtype])
     x, wg, w1, w3, w2 = (t.cuda() for t in (inp.x, inp.wg, inp.w1, inp.w3, inp.w2))
     y, idx, gate, counts = moe.moe_layer_forward(desc, x, wg, w1, w3, w2,
                                                  residual=None if residual is None else residual.cuda())
@@ -113,16 +113,17 @@ def routed_layer(counts, d, F, seed):
     times each (distinct, as every count is under T), marked by x[t, a] = 1.0
     and x[t, b] = 0.9 on top of small noise, with W_g[e, e] = 10 (other entries
     small).  The two chosen logits lead the others by about 8, so the routing
-    and its order are exact; the gates are softmax(10, 9)."""
+    and its order are exact; the gates are softmax(10, 9).  n = len(counts)."""
+    n = len(counts)
     T = sum(counts) // 2
-    inp = mi.make_layer(T, d, F, seed=seed, workload=306)
-    ids = np.repeat(np.arange(8), counts)
+    inp = mi.make_layer(T, d, F, n=n, seed=seed, workload=306 if n == 8 else 307)
+    ids = np.repeat(np.arange(n), counts)
     a, b = ids[:T], ids[T:]
     x = inp.x.float() * 0.1
     x[np.arange(T), a] = 1.0
     x[np.arange(T), b] = 0.9
     wg = inp.wg.clone()
-    wg[np.arange(8), np.arange(8)] = 10.0
+    wg[np.arange(n), np.arange(n)] = 10.0
     inp.x, inp.wg = x.to(inp.x.dtype), wg
     return inp
 
@@ -142,6 +143,28 @@ def test_layer_down_long_tails(F):
     assert down_plan(counts, d, F, T) == (1, TAIL_ROWS)
     err = check_full(inp, TOL_BF16)
     print(f"down long tails, F={F}: counts {counts}, max per-token rel err {err:.3e}")
+
+
+# Sixteen experts with the tiled kernels' full tiles, the tail pass and the K
+# split: every expert lane of the device-side tile deal, the down projection's
+# plan and the combine's expert search is a real segment.  Three experts get
+# 70-100-row tails past two full tiles, which the pass takes (35 x 16 tiles
+# against 32 x 16: three rounds against two); one expert's 144-row tail is too
+# long for the pass, and 17 x 16 tiles in halves of K fill three rounds of half
+# the length against two full ones, so the plan cuts K in two.
+@pytest.mark.parametrize("counts,F,plan", [
+    ([612, 602, 582] + [512] * 13, 1536, (1, TAIL_ROWS)),
+    ([400] + [256] * 15, 2048, (2, 0)),
+])
+def test_layer_16_experts_tails_and_split(counts, F, plan):
+    d = 4096
+    inp = routed_layer(counts, d, F, seed=F + len(counts))
+    T = inp.x.shape[0]
+    got = np.bincount(oracle.gating(inp.x.float().numpy(), inp.wg.numpy())[1].ravel(), minlength=16)
+    np.testing.assert_array_equal(got, counts)
+    assert down_plan(counts, d, F, T, n=16) == plan
+    err = check_full(inp, TOL_BF16)
+    print(f"16 experts, plan {plan}: max per-token rel err {err:.3e}")
 
 
 def test_tiny_workload():
